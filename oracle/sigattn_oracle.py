@@ -1,0 +1,367 @@
+"""Sigmoid attention oracle: a plain, slow, obviously correct fp64 CPU reference.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check in ``__graft_entry__`` and
+the CPU-baseline leg of ``bench.py`` may import or call this module. The product path
+(the HIP library under ``sigmoid_attention_amd/`` and its Python binding) never imports,
+calls or links anything here, and this module imports nothing from it.
+
+What is computed, and where it comes from
+-----------------------------------------
+Sources are three web pages:
+
+* [SA-bio] "Better Models, Faster Training: Sigmoid Attention for single-cell Foundation
+  Models" (arXiv 2604.27124): §3 "Sigmoid Attention" display equation
+  (O = sigma(Q K^T / sqrt(d) + b) V, element-wise), §4 "Block-sparse computation"
+  (fully padded query and key blocks contribute nothing), appendix A.1.2 (the Jacobian
+  of the element-wise sigmoid is diagonal with entries sigma(1 - sigma)).
+* [SA-bio-nl] the gist.science summary of the same paper (in Dutch), §2A "Sigmoid
+  Attention Mechanisme": sigma(x) = 1/(1 + e^-x) and the bias b = -log(n).
+* [KV-evict] "Sigmoid Attention as a Better Substrate for Learned KV Cache Eviction"
+  (arXiv 2608.23296), gate paragraphs: a token-wise gate g_j enters through both the
+  logits (+ log(g_j + eps), eps = 1e-8) and the values (g_j * v_j); hard deletion drops
+  keys with g_j < tau; the random-removal probe excludes the first four positions and
+  treats a removed key as masked out of the logits with its value zeroed.
+
+Readings taken where the pages are silent (each is also listed in the design notes):
+
+* n in b = -log(n) is the sequence's valid (unpadded) length, natural log, the same for
+  every query of that sequence (also under the causal mask). n = 1 gives b = 0; n = 0
+  produces all-zero outputs and b is never evaluated.
+* Padded query rows of O, dQ, dK, dV are exactly zero; padded keys contribute exactly
+  zero whatever the padded slots hold.
+* Causal means key j is allowed for query i iff j <= i.
+* Gate: x_ij += log(g_j + eps) and V'_j = g_j * v_j; the gate is per key, shared by all
+  heads. A key is dropped iff j >= sink and g_j < tau; a dropped key is treated exactly
+  like padding.
+* The backward follows from the forward by the chain rule with the diagonal Jacobian:
+  dV'_j = sum_i P_ij dO_i (so dV_j = g_j sum_i P_ij dO_i), dP_ij = dO_i . V'_j,
+  dS_ij = dP_ij P_ij (1 - P_ij), dQ_i = s sum_j dS_ij k_j, dK_j = s sum_i dS_ij q_i.
+
+All arithmetic is float64 on whatever values are passed in (the GPU's bf16 inputs are
+passed here widened, so both sides see the same bits). Library primitives used as steps:
+numpy matmul and exp. No blocking or fusion beyond splitting query rows into chunks to
+bound memory, which does not change any value beyond summation order in fp64.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+GATE_EPS = 1e-8  # [KV-evict] gate paragraph: eps avoids log 0
+DEFAULT_SINK = 4  # [KV-evict] removal probe: the first four positions are never removed
+
+__all__ = [
+    "GATE_EPS",
+    "DEFAULT_SINK",
+    "logistic",
+    "logistic_tanh",
+    "sequence_bias",
+    "kept_keys",
+    "forward",
+    "backward",
+    "forward_rows",
+    "dq_rows",
+    "dkdv_rows",
+    "forward_naive",
+    "backward_naive",
+]
+
+
+# ----------------------------------------------------------------------------------
+# scalar definitions
+# ----------------------------------------------------------------------------------
+
+def logistic(x):
+    """sigma(x) = 1 / (1 + e^-x)  ([SA-bio-nl] §2A), evaluated without overflow.
+
+    For x >= 0 the defining form is used directly; for x < 0 the algebraically equal
+    e^x / (1 + e^x) is used so that e^-x never overflows.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def logistic_tanh(x):
+    """The tanh form 0.5 * (tanh(x/2) + 1) that [SA-bio] §4 "Fused operations" uses.
+
+    It is an exact identity for sigma; kept as an independent second formula.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (np.tanh(0.5 * x) + 1.0)
+
+
+def sequence_bias(n: int) -> float:
+    """b = -log(n) for a sequence of n valid tokens ([SA-bio-nl] §2A); natural log."""
+    if n < 1:
+        raise ValueError("the bias is only defined for n >= 1")
+    return -math.log(n)
+
+
+def kept_keys(n: int, L: int, gate=None, tau: float = 0.0, sink: int = DEFAULT_SINK):
+    """Boolean [L]: key j takes part iff it is valid (j < n) and, when gated, not dropped.
+
+    Dropping ([KV-evict] hard-deletion rule): j >= sink and g_j < tau.
+    """
+    keep = np.zeros(L, dtype=bool)
+    keep[:n] = True
+    if gate is not None and tau > 0.0:
+        g = np.asarray(gate, dtype=np.float64)[:L]
+        j = np.arange(L)
+        keep &= ~((j >= sink) & (g < tau))
+    return keep
+
+
+# ----------------------------------------------------------------------------------
+# per-head building blocks
+# ----------------------------------------------------------------------------------
+
+def _params(d, scale):
+    return (1.0 / math.sqrt(d)) if (scale is None or scale == 0.0) else float(scale)
+
+
+def _head_setup(b, n, L, gate, tau, sink, bias, eps):
+    """Per-sequence quantities: beta, the key-keep mask and the per-key log-gate term."""
+    beta = sequence_bias(n) if bias is None else float(bias[b])
+    g = None if gate is None else np.asarray(gate[b], dtype=np.float64)
+    keep = kept_keys(n, L, g, tau, sink)
+    logg = np.zeros(L) if g is None else np.log(g + eps)
+    return beta, g, keep, logg
+
+
+def _allowed(rows, cols, keep, causal):
+    """allowed[i, j]: key cols[j] is kept and (bidirectional or cols[j] <= rows[i])."""
+    a = np.broadcast_to(keep[cols][None, :], (len(rows), len(cols))).copy()
+    if causal:
+        a &= cols[None, :] <= rows[:, None]
+    return a
+
+
+def _P(qr, kh, rows, cols, s, beta, logg, keep, causal):
+    """P[i, j] = sigma(s q_i.k_j + beta + log(g_j + eps)) where allowed, else exactly 0."""
+    x = s * (qr @ kh.T) + beta + logg[cols][None, :]
+    allowed = _allowed(rows, cols, keep, causal)
+    P = np.zeros_like(x)
+    P[allowed] = logistic(x[allowed])
+    return P
+
+
+def _vprime(vh, g, cols):
+    return vh if g is None else vh * g[cols][:, None]
+
+
+# ----------------------------------------------------------------------------------
+# full forward / backward
+# ----------------------------------------------------------------------------------
+
+def _as64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def forward(q, k, v, seqlens, causal=False, gate=None, tau=0.0, sink=DEFAULT_SINK,
+            eps=GATE_EPS, scale=None, bias=None, chunk=512):
+    """O[b,h] = sigma(s Q K^T + b_b [+ log(g+eps)]) V' over valid, kept keys.
+
+    q, k, v: [B, H, L, d]; seqlens: [B]; gate: [B, L] or None.
+    Returns float64 [B, H, L, d]; rows i >= n_b are exactly 0.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, L, d = q.shape
+    s = _params(d, scale)
+    O = np.zeros((B, H, L, d))
+    for b in range(B):
+        n = int(seqlens[b])
+        if n == 0:
+            continue
+        beta, g, keep, logg = _head_setup(b, n, L, gate, tau, sink, bias, eps)
+        cols = np.arange(n)
+        for h in range(H):
+            kh, vp = k[b, h, :n], _vprime(v[b, h, :n], g, cols)
+            for r0 in range(0, n, chunk):
+                rows = np.arange(r0, min(n, r0 + chunk))
+                P = _P(q[b, h, rows], kh, rows, cols, s, beta, logg, keep, causal)
+                O[b, h, rows] = P @ vp
+    return O
+
+
+def backward(q, k, v, do, seqlens, causal=False, gate=None, tau=0.0, sink=DEFAULT_SINK,
+             eps=GATE_EPS, scale=None, bias=None, chunk=512):
+    """Gradients (dQ, dK, dV) of sum(dO * O) with respect to q, k and the caller's v.
+
+    dV_j = g_j sum_i P_ij dO_i; dS_ij = (dO_i . V'_j) P_ij (1 - P_ij);
+    dQ_i = s sum_j dS_ij k_j; dK_j = s sum_i dS_ij q_i. dO rows of padded queries are
+    ignored; rows of padded or dropped keys and padded queries are exactly 0.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, H, L, d = q.shape
+    s = _params(d, scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        n = int(seqlens[b])
+        if n == 0:
+            continue
+        beta, g, keep, logg = _head_setup(b, n, L, gate, tau, sink, bias, eps)
+        cols = np.arange(n)
+        for h in range(H):
+            kh, vp = k[b, h, :n], _vprime(v[b, h, :n], g, cols)
+            dvp = np.zeros((n, d))
+            dkh = np.zeros((n, d))
+            for r0 in range(0, n, chunk):
+                rows = np.arange(r0, min(n, r0 + chunk))
+                qr, dor = q[b, h, rows], do[b, h, rows]
+                P = _P(qr, kh, rows, cols, s, beta, logg, keep, causal)
+                dP = dor @ vp.T
+                dS = dP * P * (1.0 - P)
+                dq[b, h, rows] = s * (dS @ kh)
+                dkh += s * (dS.T @ qr)
+                dvp += P.T @ dor
+            dk[b, h, :n] = dkh
+            dv[b, h, :n] = dvp if g is None else dvp * g[:n, None]
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------------
+# sampled rows (for checking large problems one output row at a time)
+# ----------------------------------------------------------------------------------
+
+def forward_rows(q, k, v, seqlens, b, h, rows, causal=False, gate=None, tau=0.0,
+                 sink=DEFAULT_SINK, eps=GATE_EPS, scale=None, bias=None):
+    """O[b, h, rows] computed from the full keys of (b, h); padded rows give 0."""
+    rows = np.asarray(rows, dtype=np.int64)
+    d = q.shape[-1]
+    out = np.zeros((len(rows), d))
+    n = int(seqlens[b])
+    if n == 0:
+        return out
+    s = _params(d, scale)
+    beta, g, keep, logg = _head_setup(b, n, q.shape[2], gate, tau, sink, bias, eps)
+    cols = np.arange(n)
+    live = rows < n
+    r = rows[live]
+    kh, vp = _as64(k[b, h, :n]), _vprime(_as64(v[b, h, :n]), g, cols)
+    P = _P(_as64(q[b, h, r]), kh, r, cols, s, beta, logg, keep, causal)
+    out[live] = P @ vp
+    return out
+
+
+def dq_rows(q, k, v, do, seqlens, b, h, rows, causal=False, gate=None, tau=0.0,
+            sink=DEFAULT_SINK, eps=GATE_EPS, scale=None, bias=None):
+    """dQ[b, h, rows]; padded rows give 0."""
+    rows = np.asarray(rows, dtype=np.int64)
+    d = q.shape[-1]
+    out = np.zeros((len(rows), d))
+    n = int(seqlens[b])
+    if n == 0:
+        return out
+    s = _params(d, scale)
+    beta, g, keep, logg = _head_setup(b, n, q.shape[2], gate, tau, sink, bias, eps)
+    cols = np.arange(n)
+    live = rows < n
+    r = rows[live]
+    kh, vp = _as64(k[b, h, :n]), _vprime(_as64(v[b, h, :n]), g, cols)
+    P = _P(_as64(q[b, h, r]), kh, r, cols, s, beta, logg, keep, causal)
+    dS = (_as64(do[b, h, r]) @ vp.T) * P * (1.0 - P)
+    out[live] = s * (dS @ kh)
+    return out
+
+
+def dkdv_rows(q, k, v, do, seqlens, b, h, key_rows, causal=False, gate=None, tau=0.0,
+              sink=DEFAULT_SINK, eps=GATE_EPS, scale=None, bias=None):
+    """(dK[b, h, key_rows], dV[b, h, key_rows]) from all valid queries of (b, h)."""
+    key_rows = np.asarray(key_rows, dtype=np.int64)
+    d = q.shape[-1]
+    dk_out = np.zeros((len(key_rows), d))
+    dv_out = np.zeros((len(key_rows), d))
+    n = int(seqlens[b])
+    if n == 0:
+        return dk_out, dv_out
+    s = _params(d, scale)
+    beta, g, keep, logg = _head_setup(b, n, q.shape[2], gate, tau, sink, bias, eps)
+    live = key_rows < n
+    cols = key_rows[live]
+    rows = np.arange(n)
+    qh, doh = _as64(q[b, h, :n]), _as64(do[b, h, :n])
+    kc, vc = _as64(k[b, h, cols]), _as64(v[b, h, cols])
+    vpc = vc if g is None else vc * g[cols][:, None]
+    P = _P(qh, kc, rows, cols, s, beta, logg, keep, causal)   # [n, len(cols)]
+    dS = (doh @ vpc.T) * P * (1.0 - P)
+    dk_out[live] = s * (dS.T @ qh)
+    dvp = P.T @ doh
+    dv_out[live] = dvp if g is None else dvp * g[cols][:, None]
+    return dk_out, dv_out
+
+
+# ----------------------------------------------------------------------------------
+# naive scalar loops (tiny inputs only): a second, structurally different reading
+# ----------------------------------------------------------------------------------
+
+def _sig_scalar(x: float) -> float:
+    if x >= 0.0:
+        return 1.0 / (1.0 + math.exp(-x))
+    e = math.exp(x)
+    return e / (1.0 + e)
+
+
+def forward_naive(q, k, v, seqlens, causal=False, gate=None, tau=0.0,
+                  sink=DEFAULT_SINK, eps=GATE_EPS):
+    """Triple loop over (query, key, feature) with scalar math; tiny inputs only."""
+    B, H, L, d = np.shape(q)
+    s = 1.0 / math.sqrt(d)
+    O = np.zeros((B, H, L, d))
+    for b in range(B):
+        n = int(seqlens[b])
+        for h in range(H):
+            for i in range(n):
+                for j in range(n):
+                    if causal and j > i:
+                        continue
+                    gj = 1.0 if gate is None else float(gate[b][j])
+                    if gate is not None and tau > 0.0 and j >= sink and gj < tau:
+                        continue
+                    dot = 0.0
+                    for c in range(d):
+                        dot += float(q[b][h][i][c]) * float(k[b][h][j][c])
+                    x = s * dot - math.log(n)
+                    if gate is not None:
+                        x += math.log(gj + eps)
+                    p = _sig_scalar(x)
+                    for c in range(d):
+                        O[b, h, i, c] += p * gj * float(v[b][h][j][c])
+    return O
+
+
+def backward_naive(q, k, v, do, seqlens, causal=False, gate=None, tau=0.0,
+                   sink=DEFAULT_SINK, eps=GATE_EPS):
+    """Scalar loops for dQ, dK, dV; tiny inputs only."""
+    B, H, L, d = np.shape(q)
+    s = 1.0 / math.sqrt(d)
+    dq, dk, dv = np.zeros((B, H, L, d)), np.zeros((B, H, L, d)), np.zeros((B, H, L, d))
+    for b in range(B):
+        n = int(seqlens[b])
+        for h in range(H):
+            for i in range(n):
+                for j in range(n):
+                    if causal and j > i:
+                        continue
+                    gj = 1.0 if gate is None else float(gate[b][j])
+                    if gate is not None and tau > 0.0 and j >= sink and gj < tau:
+                        continue
+                    dot = sum(float(q[b][h][i][c]) * float(k[b][h][j][c]) for c in range(d))
+                    x = s * dot - math.log(n)
+                    if gate is not None:
+                        x += math.log(gj + eps)
+                    p = _sig_scalar(x)
+                    dpij = sum(float(do[b][h][i][c]) * gj * float(v[b][h][j][c])
+                               for c in range(d))
+                    dsij = dpij * p * (1.0 - p)
+                    for c in range(d):
+                        dq[b, h, i, c] += s * dsij * float(k[b][h][j][c])
+                        dk[b, h, j, c] += s * dsij * float(q[b][h][i][c])
+                        dv[b, h, j, c] += gj * p * float(do[b][h][i][c])
+    return dq, dk, dv
