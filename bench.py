@@ -1,0 +1,219 @@
+"""Benchmark: effective TFLOPS of padded bf16 sigmoid attention (forward + backward) on
+one MI355X, the fp64 CPU oracle timed beside it.
+
+One step = one pass of the whole hot path over one batch: sigattn_fwd, sigattn_bwd_dq
+and sigattn_bwd_dkdv. FLOPs are counted over valid tokens only: 4 d per valid
+(query, key) pair forward, 2.5x that backward (the FLOP appendix of "Better Models,
+Faster Training: Sigmoid Attention for single-cell Foundation Models"), n^2 pairs per
+head bidirectional, n(n+1)/2 causal. Inputs are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_8k_s1]
+                    [--no-cpu-baseline]
+
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective fwd/bwd TFLOPS, bf16 padded sigmoid attn, L=8K; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+# algorithmic MFMA FLOPs per valid pair, per pass: forward S and P.V (2 x 2d); the dQ pass
+# recomputes S, forms dP and dQ (3 x 2d); the dK/dV pass recomputes S, forms dP, dV, dK
+# (4 x 2d). The credited backward (2.5 x forward = 10 d) counts S and dP once.
+PASS_FLOPS_PER_PAIR = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long_8k_s1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fast-math", action="store_true",
+                    help="time the single-bf16 operand mode instead of the default hi+lo split")
+    ap.add_argument("--bf16-out", action="store_true", help="bf16 outputs instead of float")
+    ap.add_argument("--also-fast", action="store_true",
+                    help="also time fast math with bf16 outputs and report it beside the default")
+    ap.add_argument("--cpu-sample-heads", type=int, default=2)
+    return ap.parse_args()
+
+
+def cpu_baseline(data, w, heads):
+    """Time the oracle, as it stands, on a bounded sample of the same workload: full
+    forward + backward of `heads` (b, h) pairs taken from the batch entry with the median
+    length, on the host cores."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    sl = data["seqlens"]
+    b = int(np.argsort(sl)[len(sl) // 2])
+    n = int(sl[b])
+    H = min(heads, w.H)
+    q = data["q"][b:b + 1, :H].astype(np.float64)
+    k = data["k"][b:b + 1, :H].astype(np.float64)
+    v = data["v"][b:b + 1, :H].astype(np.float64)
+    do = data["do"][b:b + 1, :H].astype(np.float64)
+    kw = dict(causal=w.causal)
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, [n], **kw)
+    t1 = time.perf_counter()
+    oracle.backward(q, k, v, do, [n], **kw)
+    t2 = time.perf_counter()
+    pairs = (n * (n + 1) // 2 if w.causal else n * n) * H
+    flops = 4.0 * w.d * pairs * 3.5   # forward + credited backward
+    return {
+        "value": flops / (t2 - t0) / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle, forward+backward of {H} heads of batch entry {b} "
+                  f"(n={n}) of {w.name}; fwd {t1 - t0:.2f} s, bwd {t2 - t1:.2f} s",
+        "host": platform.processor() or platform.machine(),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path needs no "
+              "collectives and every (batch, head) is independent; run one process per GPU "
+              "with its own share of the batch.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sigmoid_attention_amd as S
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    S.load()
+    w = W.WORKLOADS[args.workload]
+    data = W.generate(w)
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(data[k]).to(torch.bfloat16).to(dev) for k in ("q", "k", "v", "do")}
+    gate = None if data["gate"] is None else torch.from_numpy(data["gate"]).to(dev)
+    sl = data["seqlens"]
+    stream = torch.cuda.current_stream(dev)
+    out_dtype = torch.bfloat16 if args.bf16_out else torch.float32
+    mode = {"inputs": "bf16", "outputs": "bf16" if args.bf16_out else "float32",
+            "operands": "bf16" if args.fast_math else "bf16 hi+lo split"}
+    res = measure(S, W, w, t, gate, sl, stream, args.steps, args.warmup, out_dtype,
+                  args.fast_math)
+    res["mode"] = mode
+    if args.also_fast:
+        fast = measure(S, W, w, t, gate, sl, stream, args.steps, args.warmup,
+                       torch.bfloat16, True)
+        res["fast_math_bf16_out"] = {k_: fast[k_] for k_ in ("value", "ms_per_step", "fwd_tflops",
+                                                             "bwd_tflops", "fwd_pct_peak", "kernels")}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(data, w, args.cpu_sample_heads)
+    print(json.dumps(res))
+
+
+def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):
+    import torch
+    kw = dict(causal=w.causal, gate=gate, tau=w.tau, sink=w.sink, out_dtype=out_dtype,
+              fast_math=fast_math)
+    o = torch.empty(t["q"].shape, dtype=out_dtype, device=t["q"].device)
+    dq = torch.empty_like(o)
+    dk = torch.empty_like(o)
+    dv = torch.empty_like(o)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        S.fwd(t["q"], t["k"], t["v"], sl, out=o, **kw)
+        if evs is not None:
+            evs[1].record(stream)
+        S.bwd_dq(t["q"], t["k"], t["v"], t["do"], sl, out=dq, **kw)
+        if evs is not None:
+            evs[2].record(stream)
+        S.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], sl, out=(dk, dv), **kw)
+        if evs is not None:
+            evs[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / steps
+    per = {"fwd": [], "bwd_dq": [], "bwd_dkdv": []}
+    for e in evs:
+        per["fwd"].append(e[0].elapsed_time(e[1]))
+        per["bwd_dq"].append(e[1].elapsed_time(e[2]))
+        per["bwd_dkdv"].append(e[2].elapsed_time(e[3]))
+
+    f_fwd = W.flops_forward(sl, w.H, w.d, w.causal)
+    f_bwd = W.flops_backward(sl, w.H, w.d, w.causal)
+    pairs = W.valid_pairs(sl, w.causal) * w.H
+    fwd_ms = float(np.mean(per["fwd"]))
+    bwd_ms = float(np.mean(per["bwd_dq"])) + float(np.mean(per["bwd_dkdv"]))
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    kernels = {}
+    for name, times in per.items():
+        ms = float(np.mean(times))
+        algo = PASS_FLOPS_PER_PAIR[name] * w.d * pairs
+        kernels[name] = {"avg_ms": ms, "algorithmic_tflop": algo / 1e12,
+                         "achieved_tflops": algo / (ms * 1e-3) / 1e12,
+                         "frac_of_peak": algo / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    dom = max(kernels, key=lambda k_: kernels[k_]["avg_ms"])
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "Lmax": w.L,
+                   "seqlens": [int(x) for x in sl], "causal": w.causal,
+                   "gated": w.gate is not None, "seed": w.seed,
+                   "step": "sigattn_fwd + sigattn_bwd_dq + sigattn_bwd_dkdv"},
+        "fwd_tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
+        "fwd_pct_peak": 100.0 * f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "bwd_pct_peak": 100.0 * f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": dom,
+                     "achieved": kernels[dom]["achieved_tflops"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": kernels[dom]["frac_of_peak"], "traffic": None},
+        "kernels": kernels,
+    }
+    return res
+
+
+if __name__ == "__main__":
+    main()

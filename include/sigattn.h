@@ -1,0 +1,129 @@
+/*
+ * sigattn.h - C ABI of the MI355X (gfx950) padded sigmoid-attention library.
+ *
+ * Operation (per batch entry b with n = seqlens[b] valid tokens, per head h):
+ *
+ *   x_ij  = s * (q_i . k_j) + beta_b [+ log(g_j + eps)]        i, j < n
+ *   P_ij  = 1 / (1 + e^{-x_ij})   if key j is kept and (not causal or j <= i), else 0
+ *   O_i   = sum_j P_ij * V'_j,    V'_j = g_j * v_j when gated, else v_j
+ *
+ * with s = 1/sqrt(d) and beta_b = -ln(n). Sources: "Better Models, Faster Training:
+ * Sigmoid Attention for single-cell Foundation Models" (arXiv 2604.27124), section 3
+ * "Sigmoid Attention" equation (element-wise sigmoid of the scaled scores plus a bias,
+ * times V) and section 4 (block-sparse skipping of padded blocks, backward split into a
+ * dQ pass and a dK/dV pass with recomputation); its gist.science summary, section 2A,
+ * for sigma(x) = 1/(1+e^-x) and b = -log(n); and "Sigmoid Attention as a Better
+ * Substrate for Learned KV Cache Eviction" (arXiv 2608.23296), gate paragraphs, for
+ * the per-key gate (log g on the logits, g on the values, eps = 1e-8), the hard-drop
+ * rule g_j < tau and the leading positions that are never removed.
+ *
+ * Backward, from the diagonal Jacobian of the element-wise sigmoid (first paper,
+ * appendix A.1.2), given dO:
+ *   dV_j = g_j sum_i P_ij dO_i          dS_ij = (dO_i . V'_j) * P_ij (1 - P_ij)
+ *   dQ_i = s sum_j dS_ij k_j            dK_j  = s sum_i dS_ij q_i
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors q, k, v, o, dO, dq, dk, dv are [B][H][Lmax][d] views described by the
+ *    element strides stride_b, stride_h, stride_l (the last dimension is contiguous);
+ *    all of them use the same strides, counted in elements of their own type. Input
+ *    type (q, k, v, dO): bf16 (SIGATTN_BF16) or float (SIGATTN_F32, a slow debug
+ *    path). Output type (o, dq, dk, dv): out_dtype, bf16 or float; float inputs
+ *    require float outputs. Accumulation is always float.
+ *  - Precision of the bf16 path. The attention weights P and the score gradients dS
+ *    are formed in float and enter the second product of each pass as bf16 operands
+ *    of the matrix cores. With fast_math = 0 (the default) each is carried as an
+ *    unevaluated sum hi + lo of two bf16 values (about 16 significant bits; two
+ *    matrix-core products instead of one), so that the result is limited by the
+ *    bf16 inputs and the output type only. With fast_math = 1 a single bf16 value is
+ *    used (relative rounding 2^-9 per weight) and the products cost half as much.
+ *  - seqlens and bias are HOST arrays of length B, read during the call only.
+ *    gate is a DEVICE array of floats, gate[b * gate_stride_b + j], j < Lmax.
+ *  - The caller owns every buffer. The library never allocates, frees or
+ *    synchronises; it needs no workspace. Work is enqueued on `stream` (a hipStream_t;
+ *    NULL is the default stream) and the results are valid once that stream has
+ *    completed it. Identical inputs give bitwise-identical outputs (no atomics).
+ *  - Outputs are fully written: rows i >= n of O and dQ, rows j >= n of dK and dV,
+ *    and the dK/dV rows of dropped keys are exactly 0. Values in padded input slots
+ *    are never read. Inputs are not modified; outputs must not alias inputs.
+ *  - Arguments are checked on the host before anything is enqueued. On any error the
+ *    call returns a non-zero status and enqueues nothing. A failed launch returns
+ *    SIGATTN_ERR_HIP (from hipGetLastError; no synchronisation).
+ *  - Every function is thread-safe, never aborts and never prints.
+ */
+#ifndef SIGATTN_H
+#define SIGATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SIGATTN_VERSION 2
+#define SIGATTN_MAX_BATCH 256      /* B above this returns SIGATTN_ERR_UNSUPPORTED */
+#define SIGATTN_MAX_LEN 65535      /* Lmax above this returns SIGATTN_ERR_UNSUPPORTED */
+
+typedef enum {
+  SIGATTN_OK = 0,
+  SIGATTN_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, length out of range, aliasing */
+  SIGATTN_ERR_UNSUPPORTED = 2,   /* d not in {64,128}, B or Lmax above the caps, dtypes */
+  SIGATTN_ERR_ALIGNMENT = 3,     /* a base pointer or a row stride is not 16-byte aligned */
+  SIGATTN_ERR_HIP = 4            /* the HIP runtime reported an error at launch */
+} sigattn_status;
+
+typedef enum { SIGATTN_BF16 = 0, SIGATTN_F32 = 1 } sigattn_dtype;
+
+typedef struct sigattn_problem {
+  uint32_t struct_size;          /* sizeof(sigattn_problem): ABI check */
+  int32_t B, H, Lmax, d;         /* 0 <= B <= 256, H >= 1, 1 <= Lmax <= 65535, d in {64,128} */
+  int32_t dtype;                 /* sigattn_dtype of q, k, v, dO */
+  int32_t out_dtype;             /* sigattn_dtype of o, dq, dk, dv (F32 when dtype is F32) */
+  int32_t fast_math;             /* 0: hi+lo split operands (default); 1: single bf16 */
+  int64_t stride_b, stride_h, stride_l;  /* element strides, >= 0; stride_l >= d */
+  const int32_t* seqlens;        /* HOST [B]: valid length n_b, 0 <= n_b <= Lmax */
+  int32_t causal;                /* 0: bidirectional; 1: key j allowed for query i iff j <= i */
+  float scale;                   /* s; 0 selects 1/sqrt(d) */
+  const float* bias;             /* HOST [B] or NULL: NULL selects beta_b = -ln(n_b) */
+  const float* gate;             /* DEVICE floats or NULL (no gate) */
+  int64_t gate_stride_b;         /* elements between batch rows of gate; 0 selects Lmax */
+  float gate_eps;                /* added inside the log: 1e-8 in the pages; >= 0 */
+  float gate_tau;                /* key j dropped iff j >= gate_sink and g_j < gate_tau */
+  int32_t gate_sink;             /* leading positions never dropped (4 in the pages) */
+} sigattn_problem;
+
+/* Check a problem description on the host; touches no GPU. */
+sigattn_status sigattn_validate(const sigattn_problem* p);
+
+/* Forward: o = sigmoid attention of (q, k, v). Rows i >= n_b of o are written as 0.
+ * Paper: section 3 equation; fully padded query and key tiles are never computed
+ * (section 4, block-sparse computation). */
+sigattn_status sigattn_fwd(const sigattn_problem* p, const void* q, const void* k,
+                           const void* v, void* o, void* stream);
+
+/* Backward, query side: dq = s sum_j dS_ij k_j, recomputing P (no stored attention).
+ * Rows i >= n_b of dq are written as 0. Paper: section 4, backward decomposition. */
+sigattn_status sigattn_bwd_dq(const sigattn_problem* p, const void* q, const void* k,
+                              const void* v, const void* dout, void* dq, void* stream);
+
+/* Backward, key side: dk = s sum_i dS_ij q_i and dv = g_j sum_i P_ij dO_i, recomputing
+ * P; each key row is owned by one workgroup, so no atomics are used. Rows j >= n_b and
+ * rows of dropped keys are written as 0. Paper: section 4, backward decomposition. */
+sigattn_status sigattn_bwd_dkdv(const sigattn_problem* p, const void* q, const void* k,
+                                const void* v, const void* dout, void* dk, void* dv,
+                                void* stream);
+
+/* Host-side view of the work list a pass launches, for inspection and tests.
+ * pass: 0 forward, 1 dq, 2 dk/dv. Writes up to `cap` items as (b, h, tile) int32
+ * triples into `items` (may be NULL when cap is 0) in launch order, and the tile
+ * height in rows into *tile_rows (may be NULL). Returns the number of compute items,
+ * or -1 if the problem is invalid. Fully padded tiles never appear. */
+int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int64_t cap,
+                     int32_t* tile_rows);
+
+const char* sigattn_status_string(sigattn_status s);
+int sigattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SIGATTN_H */

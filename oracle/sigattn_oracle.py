@@ -191,12 +191,16 @@ def forward(q, k, v, seqlens, causal=False, gate=None, tau=0.0, sink=DEFAULT_SIN
 
 
 def backward(q, k, v, do, seqlens, causal=False, gate=None, tau=0.0, sink=DEFAULT_SINK,
-             eps=GATE_EPS, scale=None, bias=None, chunk=512):
+             eps=GATE_EPS, scale=None, bias=None, chunk=512, absolute=False):
     """Gradients (dQ, dK, dV) of sum(dO * O) with respect to q, k and the caller's v.
 
     dV_j = g_j sum_i P_ij dO_i; dS_ij = (dO_i . V'_j) P_ij (1 - P_ij);
     dQ_i = s sum_j dS_ij k_j; dK_j = s sum_i dS_ij q_i. dO rows of padded queries are
     ignored; rows of padded or dropped keys and padded queries are exactly 0.
+
+    absolute=True returns the magnitude sums of the same products instead:
+    s sum_j |dS_ij| |k_j|, s sum_i |dS_ij| |q_i| and g_j sum_i P_ij |dO_i| (element-wise
+    absolute values), which bound how rounding of dS or P propagates to each output.
     """
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
     B, H, L, d = q.shape
@@ -218,7 +222,9 @@ def backward(q, k, v, do, seqlens, causal=False, gate=None, tau=0.0, sink=DEFAUL
                 P = _P(qr, kh, rows, cols, s, beta, logg, keep, causal)
                 dP = dor @ vp.T
                 dS = dP * P * (1.0 - P)
-                dq[b, h, rows] = s * (dS @ kh)
+                if absolute:
+                    dS, qr, dor = np.abs(dS), np.abs(qr), np.abs(dor)
+                dq[b, h, rows] = s * (dS @ (np.abs(kh) if absolute else kh))
                 dkh += s * (dS.T @ qr)
                 dvp += P.T @ dor
             dk[b, h, :n] = dkh
@@ -251,8 +257,8 @@ def forward_rows(q, k, v, seqlens, b, h, rows, causal=False, gate=None, tau=0.0,
 
 
 def dq_rows(q, k, v, do, seqlens, b, h, rows, causal=False, gate=None, tau=0.0,
-            sink=DEFAULT_SINK, eps=GATE_EPS, scale=None, bias=None):
-    """dQ[b, h, rows]; padded rows give 0."""
+            sink=DEFAULT_SINK, eps=GATE_EPS, scale=None, bias=None, absolute=False):
+    """dQ[b, h, rows]; padded rows give 0. absolute=True: s sum_j |dS_ij| |k_j|."""
     rows = np.asarray(rows, dtype=np.int64)
     d = q.shape[-1]
     out = np.zeros((len(rows), d))
@@ -267,13 +273,16 @@ def dq_rows(q, k, v, do, seqlens, b, h, rows, causal=False, gate=None, tau=0.0,
     kh, vp = _as64(k[b, h, :n]), _vprime(_as64(v[b, h, :n]), g, cols)
     P = _P(_as64(q[b, h, r]), kh, r, cols, s, beta, logg, keep, causal)
     dS = (_as64(do[b, h, r]) @ vp.T) * P * (1.0 - P)
+    if absolute:
+        dS, kh = np.abs(dS), np.abs(kh)
     out[live] = s * (dS @ kh)
     return out
 
 
 def dkdv_rows(q, k, v, do, seqlens, b, h, key_rows, causal=False, gate=None, tau=0.0,
-              sink=DEFAULT_SINK, eps=GATE_EPS, scale=None, bias=None):
-    """(dK[b, h, key_rows], dV[b, h, key_rows]) from all valid queries of (b, h)."""
+              sink=DEFAULT_SINK, eps=GATE_EPS, scale=None, bias=None, absolute=False):
+    """(dK[b, h, key_rows], dV[b, h, key_rows]) from all valid queries of (b, h).
+    absolute=True: (s sum_i |dS_ij| |q_i|, g_j sum_i P_ij |dO_i|)."""
     key_rows = np.asarray(key_rows, dtype=np.int64)
     d = q.shape[-1]
     dk_out = np.zeros((len(key_rows), d))
@@ -291,6 +300,8 @@ def dkdv_rows(q, k, v, do, seqlens, b, h, key_rows, causal=False, gate=None, tau
     vpc = vc if g is None else vc * g[cols][:, None]
     P = _P(qh, kc, rows, cols, s, beta, logg, keep, causal)   # [n, len(cols)]
     dS = (doh @ vpc.T) * P * (1.0 - P)
+    if absolute:
+        dS, qh, doh = np.abs(dS), np.abs(qh), np.abs(doh)
     dk_out[live] = s * (dS.T @ qh)
     dvp = P.T @ doh
     dv_out[live] = dvp if g is None else dvp * g[cols][:, None]

@@ -1,0 +1,266 @@
+"""Padded sigmoid attention on MI355X (gfx950): Python binding of libsigattn.so.
+
+Argument marshalling only: every step runs in the HIP kernels of the library. PyTorch
+supplies device buffers and the current stream, nothing else. The library must have
+been built (``python -m sigmoid_attention_amd.build``); if it is missing every call
+raises, there is no fallback.
+
+    o = fwd(q, k, v, seqlens, causal=False, gate=None, tau=0.0, sink=4,
+            out_dtype=None, fast_math=False)
+    dq = bwd_dq(q, k, v, do, seqlens, ...)
+    dk, dv = bwd_dkdv(q, k, v, do, seqlens, ...)
+
+Tensors are [B, H, Lmax, d] views (any strides with a contiguous last dimension, the
+same strides for all of them), bf16 or float32 (the float32 debug path), on one GPU.
+``seqlens`` holds the valid length of each batch entry (host ints). ``gate`` is an
+optional [B, Lmax] float32 device tensor of per-key gates.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = ["fwd", "bwd_dq", "bwd_dkdv", "validate", "plan", "library_path", "load",
+           "Problem", "SigattnError", "STATUS", "VERSION"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsigattn.so")
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem",
+          3: "misaligned pointer or stride", 4: "HIP runtime error"}
+BF16, F32 = 0, 1
+VERSION = 2
+
+
+class SigattnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(code, 'unknown')} (status {code})")
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``sigattn_problem`` in include/sigattn.h."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Lmax", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("fast_math", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+        ("stride_l", ctypes.c_int64),
+        ("seqlens", ctypes.POINTER(ctypes.c_int32)),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("bias", ctypes.POINTER(ctypes.c_float)),
+        ("gate", ctypes.c_void_p),
+        ("gate_stride_b", ctypes.c_int64),
+        ("gate_eps", ctypes.c_float),
+        ("gate_tau", ctypes.c_float),
+        ("gate_sink", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libsigattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run python -m sigmoid_attention_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp = ctypes.c_void_p
+    lib.sigattn_validate.argtypes = [P]
+    lib.sigattn_fwd.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.sigattn_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_plan.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                 ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]
+    lib.sigattn_plan.restype = ctypes.c_int64
+    lib.sigattn_status_string.argtypes = [ctypes.c_int]
+    lib.sigattn_status_string.restype = ctypes.c_char_p
+    lib.sigattn_version.restype = ctypes.c_int
+    for f in (lib.sigattn_validate, lib.sigattn_fwd, lib.sigattn_bwd_dq, lib.sigattn_bwd_dkdv):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def make_problem(B, H, Lmax, d, seqlens, *, dtype=BF16, out_dtype=None, fast_math=False,
+                 strides=None, causal=False, scale=0.0, bias=None, gate_ptr=None,
+                 gate_stride_b=0, eps=1e-8, tau=0.0, sink=4):
+    """Build a Problem. Returns (problem, keepalive) where keepalive owns host arrays."""
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32).reshape(-1))
+    if sl.shape[0] != B:
+        raise ValueError(f"seqlens has {sl.shape[0]} entries, expected B = {B}")
+    if strides is None:
+        strides = (H * Lmax * d, Lmax * d, d)
+    p = Problem()
+    p.struct_size = ctypes.sizeof(Problem)
+    p.B, p.H, p.Lmax, p.d = B, H, Lmax, d
+    p.dtype = dtype
+    p.out_dtype = dtype if out_dtype is None else out_dtype
+    p.fast_math = 1 if fast_math else 0
+    p.stride_b, p.stride_h, p.stride_l = (int(s) for s in strides)
+    p.seqlens = sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    p.causal = 1 if causal else 0
+    p.scale = float(scale)
+    keep = [sl]
+    if bias is not None:
+        bb = np.ascontiguousarray(np.asarray(bias, dtype=np.float32).reshape(-1))
+        keep.append(bb)
+        p.bias = bb.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    p.gate = gate_ptr
+    p.gate_stride_b = int(gate_stride_b)
+    p.gate_eps = float(eps)
+    p.gate_tau = float(tau)
+    p.gate_sink = int(sink)
+    return p, keep
+
+
+def validate(problem: Problem) -> int:
+    return load().sigattn_validate(ctypes.byref(problem))
+
+
+def plan(problem: Problem, pass_: int):
+    """Work list of a pass as an int32 array [n, 3] of (b, h, tile), and the tile height."""
+    lib = load()
+    tile = ctypes.c_int32(0)
+    n = lib.sigattn_plan(ctypes.byref(problem), pass_, None, 0, ctypes.byref(tile))
+    if n < 0:
+        raise ValueError("invalid problem")
+    out = np.zeros((max(n, 1), 3), dtype=np.int32)
+    lib.sigattn_plan(ctypes.byref(problem), pass_,
+                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n, ctypes.byref(tile))
+    return out[:n], tile.value
+
+
+# ----------------------------------------------------------------------------------
+# torch-facing wrappers
+# ----------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _describe(q, tensors, seqlens, causal, gate, tau, sink, eps, scale, bias,
+              out_dtype=None, fast_math=False):
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, Lmax, d] tensors")
+    B, H, L, d = q.shape
+    for t in tensors:
+        if t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype:
+            raise ValueError("all tensors must share shape, strides and dtype")
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError("all tensors must be on the same GPU")
+    if q.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    if q.dtype == torch.bfloat16:
+        dtype = BF16
+    elif q.dtype == torch.float32:
+        dtype = F32
+    else:
+        raise ValueError("dtype must be bfloat16 or float32")
+    gate_ptr, gsb = None, 0
+    if gate is not None:
+        if gate.dtype != torch.float32 or gate.device != q.device or gate.dim() != 2:
+            raise ValueError("gate must be a float32 [B, Lmax] tensor on the same GPU")
+        if gate.stride(-1) != 1:
+            raise ValueError("gate rows must be contiguous")
+        gate_ptr, gsb = gate.data_ptr(), gate.stride(0)
+    if hasattr(seqlens, "cpu"):
+        seqlens = seqlens.cpu().numpy()
+    if out_dtype is None or out_dtype == q.dtype:
+        odt = dtype
+    elif out_dtype == torch.float32:
+        odt = F32
+    elif out_dtype == torch.bfloat16:
+        odt = BF16
+    else:
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    return make_problem(B, H, L, d, seqlens, dtype=dtype, out_dtype=odt,
+                        fast_math=fast_math, strides=q.stride()[:3], causal=causal,
+                        scale=scale, bias=bias, gate_ptr=gate_ptr, gate_stride_b=gsb,
+                        eps=eps, tau=tau, sink=sink)
+
+
+def _new_out(q, out_dtype):
+    torch = _torch()
+    dt = q.dtype if out_dtype is None else out_dtype
+    return torch.empty_strided(q.shape, q.stride(), dtype=dt, device=q.device)
+
+
+def _check_out(q, t, out_dtype):
+    dt = q.dtype if out_dtype is None else out_dtype
+    if t.shape != q.shape or t.stride() != q.stride() or t.dtype != dt or t.device != q.device:
+        raise ValueError("output tensors must match q in shape and strides, with the output dtype")
+
+
+def _stream(q):
+    return _torch().cuda.current_stream(q.device).cuda_stream
+
+
+def _check(code, what):
+    if code != 0:
+        raise SigattnError(code, what)
+
+
+def fwd(q, k, v, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, eps=1e-8,
+        scale=0.0, bias=None, out=None, out_dtype=None, fast_math=False):
+    """O = sigma(s Q K^T + b) V' over valid keys; rows past each length are 0."""
+    lib = load()
+    prob, keep = _describe(q, (k, v), seqlens, causal, gate, tau, sink, eps, scale, bias,
+                           out_dtype, fast_math)
+    if out is None:
+        out = _new_out(q, out_dtype)
+    _check_out(q, out, out_dtype)
+    code = lib.sigattn_fwd(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           out.data_ptr(), _stream(q))
+    del keep
+    _check(code, "sigattn_fwd")
+    return out
+
+
+def bwd_dq(q, k, v, do, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, eps=1e-8,
+           scale=0.0, bias=None, out=None, out_dtype=None, fast_math=False):
+    """dQ of sum(dO * O); rows past each length are 0."""
+    lib = load()
+    prob, keep = _describe(q, (k, v, do), seqlens, causal, gate, tau, sink, eps, scale, bias,
+                           out_dtype, fast_math)
+    if out is None:
+        out = _new_out(q, out_dtype)
+    _check_out(q, out, out_dtype)
+    code = lib.sigattn_bwd_dq(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              do.data_ptr(), out.data_ptr(), _stream(q))
+    del keep
+    _check(code, "sigattn_bwd_dq")
+    return out
+
+
+def bwd_dkdv(q, k, v, do, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, eps=1e-8,
+             scale=0.0, bias=None, out=None, out_dtype=None, fast_math=False):
+    """(dK, dV) of sum(dO * O); rows past each length and dropped keys are 0."""
+    lib = load()
+    prob, keep = _describe(q, (k, v, do), seqlens, causal, gate, tau, sink, eps, scale, bias,
+                           out_dtype, fast_math)
+    dk, dv = (_new_out(q, out_dtype), _new_out(q, out_dtype)) if out is None else out
+    _check_out(q, dk, out_dtype)
+    _check_out(q, dv, out_dtype)
+    code = lib.sigattn_bwd_dkdv(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                do.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream(q))
+    del keep
+    _check(code, "sigattn_bwd_dkdv")
+    return dk, dv

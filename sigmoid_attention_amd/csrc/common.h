@@ -1,0 +1,229 @@
+// Device helpers for the gfx950 (CDNA4) sigmoid-attention kernels: MFMA and LDS
+// wrappers, the swizzled LDS tile layout, register-staged tile loads, and the
+// exp2/rcp form of the logistic function.
+//
+// Lane layouts of v_mfma_f32_32x32x16_bf16 (64 lanes, l = lane):
+//   A[i][k]: lane l holds i = l % 32, k = 8*(l/32) + 0..7        (8 bf16)
+//   B[k][j]: lane l holds j = l % 32, k = 8*(l/32) + 0..7        (8 bf16)
+//   D[i][j]: lane l, register r holds i = 8*(r/4) + 4*(l/32) + r%4, j = l % 32
+// A product whose result feeds the next MFMA as an operand is computed transposed
+// (S^T = K Q^T), so each lane owns one query column and 16 keys of it; those 16
+// registers are consumed directly as the k-slots of the next MFMA, with the k-slot
+// -> key permutation  slot 8*h + m  <->  key 8*(m/4) + 4*h + m%4  (h = l/32) applied
+// identically to the other operand.
+//
+// ds_read_b64_tr_b16: within each 16-lane group, source lane j points at 4 bf16;
+// output lane 16g+m receives element (m & 3) of source lanes 16g + (m >> 2) + 4e,
+// e = 0..3. With source lane j addressing row r0 + j/4, column c0 + 4*(j%4) of a
+// row-major tile, output lane m gets rows r0..r0+3 of column c0 + m: a column read.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kargs.h"
+
+namespace sa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define SA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+// Make the compiler wait for a register's pending load here, so that loop bodies that
+// use it do not conservatively wait for every load in flight (including prefetches).
+template <typename V>
+__device__ __forceinline__ void settle(V& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// ---------------------------------------------------------------------------------
+// LDS tile layout: [rows][D] bf16, 16-byte chunks of each row XOR-swizzled by row & 7.
+// ---------------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ uint32_t swz(int row, int col) {
+  return (uint32_t)(row * (D * 2) + ((((col >> 3) ^ (row & 7))) << 4) + ((col & 7) << 1));
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const char* base, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* base, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4*)(base + off));
+}
+
+__device__ __forceinline__ bf16x8 cat(const bf16x4& a, const bf16x4& b) {
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// Column operand of a 32x32x16 MFMA from a row-major swizzled tile: lane l receives
+// rows row0 + (slot->row map) of column col0 + l%32 for the 16 k-slots of k-step
+// `ks` (rows row0 + 16*ks + 8*(m/4) + 4*(l/32) + m%4). Two transposed reads.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_col_operand(const char* tile, int row0, int col0) {
+  const int l = lane_id();
+  const int g = l >> 4, j = l & 15;
+  const int r = row0 + 4 * (g >> 1) + (j >> 2);
+  const int c = col0 + 16 * (g & 1) + 4 * (j & 3);
+  const bf16x4 lo = lds_read_tr(tile, swz<D>(r, c));
+  const bf16x4 hi = lds_read_tr(tile, swz<D>(r + 8, c));
+  return cat(lo, hi);
+}
+
+// Row operand: lane l receives row row0 + l%32, columns col0 + 8*(l/32) + 0..7.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_operand(const char* tile, int row0, int col0) {
+  const int l = lane_id();
+  return lds_read16(tile, swz<D>(row0 + (l & 31), col0 + 8 * (l >> 5)));
+}
+
+// ---------------------------------------------------------------------------------
+// Staging of a [ROWS][D] bf16 tile: 16-byte global loads into registers (issued one
+// tile ahead, so their latency hides behind the current tile's MFMA work), then
+// 16-byte LDS stores into the swizzled layout. Consecutive threads load consecutive
+// 16-byte chunks, so each wave reads whole rows. Rows past the valid length are
+// clamped to the last valid row: padded memory is never read, and the caller masks
+// those rows out of the result.
+// ---------------------------------------------------------------------------------
+template <int ROWS, int D, int NTHREADS>
+struct TileRegs {
+  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  static constexpr int ITERS = ROWS * CPR / NTHREADS;
+  static_assert(ROWS * CPR % NTHREADS == 0, "tile must split evenly over the threads");
+  u32x4 r[ITERS];
+
+  __device__ __forceinline__ void load(const bf16* src, int64_t sl, int row_base, int last_row) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int P = it * NTHREADS + (int)threadIdx.x;
+      const int row = P / CPR;
+      int grow = row_base + row;
+      grow = grow < last_row ? grow : last_row;
+      r[it] = *reinterpret_cast<const u32x4*>(src + (int64_t)grow * sl + (P % CPR) * 8);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds_tile) const {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int P = it * NTHREADS + (int)threadIdx.x;
+      *reinterpret_cast<u32x4*>(lds_tile + swz<D>(P / CPR, (P % CPR) * 8)) = r[it];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------
+// Logistic function: sigma(x) = 1 / (1 + 2^t), t = -x * log2(e) = acc * c1 + c2 with
+// c1 = -s*log2(e), c2 = -beta*log2(e). Hardware v_exp_f32 / v_rcp_f32; for large t
+// exp2 -> +inf and rcp -> 0, for very negative t exp2 -> 0 and rcp -> 1: no NaN.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ float sigmoid_l2(float acc, float c1, float c2) {
+  const float t = __builtin_fmaf(acc, c1, c2);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)v[base + i];
+  return r;
+}
+
+// Split 8 floats v[base..base+7] into bf16 hi (round to nearest even) and bf16 lo =
+// bf16(v - hi), so that hi + lo carries about 16 significant bits. The residual
+// v - hi is exact in float and is formed by one v_dot2c_f32_bf16 per element:
+// v + (hi0, hi1) . (-1, 0).
+// The two selector pairs (-1, 0) and (0, -1) live in registers, built once per kernel
+// from their bit patterns 0x0000bf80 and 0xbf800000: as an inline-constant operand of a
+// packed bf16 instruction they would not carry the intended halves.
+struct SplitSel {
+  bf16x2 m0, m1;
+  __device__ __forceinline__ SplitSel() {
+    uint32_t b0 = 0x0000bf80u, b1 = 0xbf800000u;
+    asm volatile("" : "+v"(b0), "+v"(b1));
+    m0 = __builtin_bit_cast(bf16x2, b0);
+    m1 = __builtin_bit_cast(bf16x2, b1);
+  }
+};
+
+__device__ __forceinline__ void split8(const f32x16& v, int base, bf16x8& hi, bf16x8& lo,
+                                       const SplitSel& sel) {
+  const bf16x2 m0 = sel.m0, m1 = sel.m1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = v[base + 2 * i], b = v[base + 2 * i + 1];
+    bf16x2 h;
+    h[0] = (bf16)a;
+    h[1] = (bf16)b;
+    const float ra = __builtin_amdgcn_fdot2_f32_bf16(h, m0, a, false);
+    const float rb = __builtin_amdgcn_fdot2_f32_bf16(h, m1, b, false);
+    hi[2 * i] = h[0];
+    hi[2 * i + 1] = h[1];
+    lo[2 * i] = (bf16)ra;
+    lo[2 * i + 1] = (bf16)rb;
+  }
+}
+
+// Key (or query) index held by register r of lane l in a 32x32 MFMA result, relative
+// to the tile's row 0.
+__device__ __forceinline__ int acc_row(int r, int l) { return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3); }
+
+// Store a 32-column x 32-row float accumulator tile, transposed in registers (lane l
+// owns output row `row`, registers hold 16 of the 32 columns col0 + acc_row(r, l)), as
+// bf16 with a scale: four 8-byte stores per lane.
+__device__ __forceinline__ void store_row_bf16(bf16* dst_row, const f32x16& acc, int col0,
+                                               float mul) {
+  const int l = lane_id();
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[4 * a + e] * mul);
+    *reinterpret_cast<bf16x4*>(dst_row + col0 + 8 * a + 4 * (l >> 5)) = v;
+  }
+}
+
+__device__ __forceinline__ void store_row_f32(float* dst_row, const f32x16& acc, int col0,
+                                              float mul) {
+  const int l = lane_id();
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = acc[4 * a + e] * mul;
+    *reinterpret_cast<f32x4*>(dst_row + col0 + 8 * a + 4 * (l >> 5)) = v;
+  }
+}
+
+// Store one lane's output row (bf16 or float output type, chosen at run time).
+__device__ __forceinline__ void store_row(void* base, int64_t row_off, bool out_f32,
+                                          const f32x16& acc, int col0, float mul) {
+  if (out_f32) store_row_f32(reinterpret_cast<float*>(base) + row_off, acc, col0, mul);
+  else store_row_bf16(reinterpret_cast<bf16*>(base) + row_off, acc, col0, mul);
+}
+
+}  // namespace sa

@@ -1,0 +1,285 @@
+// Host side of the C ABI declared in include/sigattn.h: argument validation, the
+// length-aware work planner (valid tiles only, longest sequences first, XCD-grouped)
+// and kernel launch on the caller's stream. Nothing here allocates, frees or
+// synchronises.
+#include "../../include/sigattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "aux_args.h"
+#include "kargs.h"
+
+namespace sa {
+hipError_t launch_fwd_bf16(const KArgs& a, int d, bool causal, bool gated, bool split, hipStream_t st);
+hipError_t launch_dq_bf16(const KArgs& a, int d, bool causal, bool gated, bool split, hipStream_t st);
+hipError_t launch_dkdv_bf16(const KArgs& a, int d, bool causal, bool gated, bool split, hipStream_t st);
+int fwd_tile_rows(int d);
+int dq_tile_rows(int d);
+int dkdv_tile_rows(int d);
+hipError_t launch_zero_rows(const ZArgs& z, int B, int H, hipStream_t st);
+hipError_t launch_f32(const DArgs& a, int pass, hipStream_t st);
+}  // namespace sa
+
+namespace {
+
+using sa::KArgs;
+
+constexpr double kLog2eD = 1.4426950408889634;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(const sigattn_problem* p) { return p->dtype == SIGATTN_BF16 ? 2 : 4; }
+int out_elem_size(const sigattn_problem* p) { return p->out_dtype == SIGATTN_BF16 ? 2 : 4; }
+
+double beta_of(const sigattn_problem* p, int b) {
+  if (p->bias) return (double)p->bias[b];
+  const int n = p->seqlens[b];
+  return n > 0 ? -std::log((double)n) : 0.0;   // b = -ln(n); unused when n = 0
+}
+
+double scale_of(const sigattn_problem* p) {
+  return p->scale != 0.0f ? (double)p->scale : 1.0 / std::sqrt((double)p->d);
+}
+
+sigattn_status validate_problem(const sigattn_problem* p) {
+  if (!p) return SIGATTN_ERR_INVALID_ARG;
+  if (p->struct_size != sizeof(sigattn_problem)) return SIGATTN_ERR_INVALID_ARG;
+  if (p->B < 0 || p->H < 1 || p->Lmax < 1) return SIGATTN_ERR_INVALID_ARG;
+  if (p->B > SIGATTN_MAX_BATCH || p->Lmax > SIGATTN_MAX_LEN) return SIGATTN_ERR_UNSUPPORTED;
+  if (p->d != 64 && p->d != 128) return SIGATTN_ERR_UNSUPPORTED;
+  if (p->dtype != SIGATTN_BF16 && p->dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
+  if (p->out_dtype != SIGATTN_BF16 && p->out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
+  if (p->dtype == SIGATTN_F32 && p->out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
+  if (p->fast_math != 0 && p->fast_math != 1) return SIGATTN_ERR_INVALID_ARG;
+  if (p->stride_b < 0 || p->stride_h < 0 || p->stride_l < p->d) return SIGATTN_ERR_INVALID_ARG;
+  if (p->B > 0 && !p->seqlens) return SIGATTN_ERR_INVALID_ARG;
+  for (int b = 0; b < p->B; ++b)
+    if (p->seqlens[b] < 0 || p->seqlens[b] > p->Lmax) return SIGATTN_ERR_INVALID_ARG;
+  if (p->causal != 0 && p->causal != 1) return SIGATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(p->scale) || p->scale < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+  if (p->bias)
+    for (int b = 0; b < p->B; ++b)
+      if (!std::isfinite(p->bias[b])) return SIGATTN_ERR_INVALID_ARG;
+  if (p->gate) {
+    if (reinterpret_cast<uintptr_t>(p->gate) & 3u) return SIGATTN_ERR_ALIGNMENT;
+    if (p->gate_stride_b < 0 || (p->gate_stride_b != 0 && p->gate_stride_b < p->Lmax))
+      return SIGATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(p->gate_eps) || p->gate_eps < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(p->gate_tau) || p->gate_tau < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+    if (p->gate_sink < 0) return SIGATTN_ERR_INVALID_ARG;
+  }
+  // every row must start on a 16-byte boundary
+  const int64_t es = elem_size(p);
+  if (((p->stride_l * es) & 15) || ((p->stride_h * es) & 15) || ((p->stride_b * es) & 15))
+    return SIGATTN_ERR_ALIGNMENT;
+  return SIGATTN_OK;
+}
+
+sigattn_status check_tensors(const void* const* in, int nin, void* const* out, int nout) {
+  for (int i = 0; i < nin; ++i) {
+    if (!in[i]) return SIGATTN_ERR_INVALID_ARG;
+    if (!aligned16(in[i])) return SIGATTN_ERR_ALIGNMENT;
+  }
+  for (int o = 0; o < nout; ++o) {
+    if (!out[o]) return SIGATTN_ERR_INVALID_ARG;
+    if (!aligned16(out[o])) return SIGATTN_ERR_ALIGNMENT;
+    for (int i = 0; i < nin; ++i)
+      if (out[o] == in[i]) return SIGATTN_ERR_INVALID_ARG;
+    for (int o2 = 0; o2 < o; ++o2)
+      if (out[o] == out[o2]) return SIGATTN_ERR_INVALID_ARG;
+  }
+  return SIGATTN_OK;
+}
+
+int tile_rows(const sigattn_problem* p, int pass) {
+  return pass == 0 ? sa::fwd_tile_rows(p->d) : pass == 1 ? sa::dq_tile_rows(p->d) : sa::dkdv_tile_rows(p->d);
+}
+
+int xcd_chunk_default() {
+  static int v = [] {
+    const char* e = std::getenv("SIGATTN_XCD_CHUNK");
+    return e ? std::atoi(e) : 16;
+  }();
+  return v;
+}
+
+// Fill the kernel-argument block of one pass: the sorted, padded-tile-free work list.
+void plan_pass(const sigattn_problem* p, int pass, KArgs* a) {
+  std::memset(a, 0, sizeof(*a));
+  const int tile = tile_rows(p, pass);
+  std::vector<int> order;
+  for (int b = 0; b < p->B; ++b)
+    if (p->seqlens[b] > 0) order.push_back(b);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return p->seqlens[x] > p->seqlens[y]; });
+  a->nsorted = (int)order.size();
+  a->off[0] = 0;
+  for (int i = 0; i < a->nsorted; ++i) {
+    const int b = order[i];
+    const int n = p->seqlens[b];
+    const int T = (n + tile - 1) / tile;
+    a->off[i + 1] = a->off[i] + p->H * T;
+    a->len[i] = (uint16_t)n;
+    a->bidx[i] = (uint8_t)b;
+    a->c2[i] = (float)(-beta_of(p, b) * kLog2eD);
+  }
+  a->nitems = a->off[a->nsorted];
+  a->H = p->H;
+  a->Lmax = p->Lmax;
+  a->tile = tile;
+  a->xcd_chunk = xcd_chunk_default();
+  a->causal = p->causal;
+  a->reverse = (p->causal && pass != 2) ? 1 : 0;
+  a->sb = p->stride_b;
+  a->sh = p->stride_h;
+  a->sl = p->stride_l;
+  const double s = scale_of(p);
+  a->scale = (float)s;
+  a->c1 = (float)(-s * kLog2eD);
+  a->gate = p->gate;
+  a->gsb = p->gate_stride_b ? p->gate_stride_b : p->Lmax;
+  a->gate_eps = p->gate_eps;
+  a->gate_tau = p->gate_tau;
+  a->gate_sink = p->gate_sink;
+  a->out_f32 = p->out_dtype == SIGATTN_F32 ? 1 : 0;
+}
+
+bool needs_zero_fill(const sigattn_problem* p) {
+  for (int b = 0; b < p->B; ++b)
+    if (p->seqlens[b] < p->Lmax) return true;
+  return false;
+}
+
+sigattn_status zero_fill(const sigattn_problem* p, void* o0, void* o1, hipStream_t st) {
+  if (!needs_zero_fill(p)) return SIGATTN_OK;
+  sa::ZArgs z;
+  std::memset(&z, 0, sizeof(z));
+  z.o0 = o0;
+  z.o1 = o1;
+  z.sb = p->stride_b;
+  z.sh = p->stride_h;
+  z.sl = p->stride_l;
+  z.Lmax = p->Lmax;
+  z.esize = out_elem_size(p);
+  z.row_bytes = p->d * z.esize;
+  for (int b = 0; b < p->B; ++b) z.len[b] = (uint16_t)p->seqlens[b];
+  return sa::launch_zero_rows(z, p->B, p->H, st) == hipSuccess ? SIGATTN_OK : SIGATTN_ERR_HIP;
+}
+
+sigattn_status run_f32(const sigattn_problem* p, int pass, const void* q, const void* k,
+                       const void* v, const void* dout, void* o0, void* o1, hipStream_t st) {
+  sa::DArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1;
+  a.gate = p->gate;
+  a.sb = p->stride_b; a.sh = p->stride_h; a.sl = p->stride_l;
+  a.gsb = p->gate_stride_b ? p->gate_stride_b : p->Lmax;
+  a.B = p->B; a.H = p->H; a.Lmax = p->Lmax; a.d = p->d;
+  a.causal = p->causal;
+  a.gate_sink = p->gate_sink;
+  a.scale = (float)scale_of(p);
+  a.gate_eps = p->gate_eps;
+  a.gate_tau = p->gate_tau;
+  for (int b = 0; b < p->B; ++b) {
+    a.len[b] = p->seqlens[b];
+    a.beta[b] = (float)beta_of(p, b);
+  }
+  if (sa::launch_f32(a, pass, st) != hipSuccess) return SIGATTN_ERR_HIP;
+  return zero_fill(p, o0, o1, st);
+}
+
+sigattn_status run_pass(const sigattn_problem* p, int pass, const void* q, const void* k,
+                        const void* v, const void* dout, void* o0, void* o1, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (p->B == 0) return SIGATTN_OK;
+  if (p->dtype == SIGATTN_F32) return run_f32(p, pass, q, k, v, dout, o0, o1, st);
+  KArgs a;
+  plan_pass(p, pass, &a);
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1;
+  const bool causal = p->causal != 0, gated = p->gate != nullptr;
+  if (a.nitems > 0) {
+    hipError_t e;
+    const bool split = p->fast_math == 0;
+    if (pass == 0) e = sa::launch_fwd_bf16(a, p->d, causal, gated, split, st);
+    else if (pass == 1) e = sa::launch_dq_bf16(a, p->d, causal, gated, split, st);
+    else e = sa::launch_dkdv_bf16(a, p->d, causal, gated, split, st);
+    if (e != hipSuccess) return SIGATTN_ERR_HIP;
+  }
+  return zero_fill(p, o0, o1, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+sigattn_status sigattn_validate(const sigattn_problem* p) { return validate_problem(p); }
+
+sigattn_status sigattn_fwd(const sigattn_problem* p, const void* q, const void* k,
+                           const void* v, void* o, void* stream) {
+  sigattn_status s = validate_problem(p);
+  if (s != SIGATTN_OK) return s;
+  const void* in[3] = {q, k, v};
+  void* out[1] = {o};
+  if ((s = check_tensors(in, 3, out, 1)) != SIGATTN_OK) return s;
+  return run_pass(p, 0, q, k, v, nullptr, o, nullptr, stream);
+}
+
+sigattn_status sigattn_bwd_dq(const sigattn_problem* p, const void* q, const void* k,
+                              const void* v, const void* dout, void* dq, void* stream) {
+  sigattn_status s = validate_problem(p);
+  if (s != SIGATTN_OK) return s;
+  const void* in[4] = {q, k, v, dout};
+  void* out[1] = {dq};
+  if ((s = check_tensors(in, 4, out, 1)) != SIGATTN_OK) return s;
+  return run_pass(p, 1, q, k, v, dout, dq, nullptr, stream);
+}
+
+sigattn_status sigattn_bwd_dkdv(const sigattn_problem* p, const void* q, const void* k,
+                                const void* v, const void* dout, void* dk, void* dv,
+                                void* stream) {
+  sigattn_status s = validate_problem(p);
+  if (s != SIGATTN_OK) return s;
+  const void* in[4] = {q, k, v, dout};
+  void* out[2] = {dk, dv};
+  if ((s = check_tensors(in, 4, out, 2)) != SIGATTN_OK) return s;
+  return run_pass(p, 2, q, k, v, dout, dk, dv, stream);
+}
+
+int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int64_t cap,
+                     int32_t* tile_rows_out) {
+  if (validate_problem(p) != SIGATTN_OK || pass < 0 || pass > 2) return -1;
+  if (cap > 0 && !items) return -1;
+  if (p->B == 0) return 0;
+  KArgs a;
+  plan_pass(p, pass, &a);
+  if (tile_rows_out) *tile_rows_out = a.tile;
+  for (int w = 0; w < a.nitems && w < cap; ++w) {
+    const sa::Item it = sa::decode_item(a, sa::remap_block(w, a.nitems, a.xcd_chunk));
+    items[3 * w + 0] = it.b;
+    items[3 * w + 1] = it.h;
+    items[3 * w + 2] = it.t;
+  }
+  return a.nitems;
+}
+
+const char* sigattn_status_string(sigattn_status s) {
+  switch (s) {
+    case SIGATTN_OK: return "ok";
+    case SIGATTN_ERR_INVALID_ARG: return "invalid argument";
+    case SIGATTN_ERR_UNSUPPORTED: return "unsupported problem";
+    case SIGATTN_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case SIGATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int sigattn_version(void) { return SIGATTN_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+"""Host-side tests of the C ABI: exported symbols, argument validation and the work
+planner. None of these launch a kernel; they run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sigmoid_attention_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sigattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(S.library_path()):
+        pytest.fail("libsigattn.so is not built (run python -m sigmoid_attention_amd.build)")
+    return S.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sigattn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for f in ("sigattn_fwd", "sigattn_bwd_dq", "sigattn_bwd_dkdv", "sigattn_validate"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_problem_struct_matches_header_size(lib):
+    # the library rejects a struct_size that differs from its own sizeof
+    p, keep = S.make_problem(1, 1, 64, 64, [64])
+    assert S.validate(p) == 0
+    p.struct_size += 8
+    assert S.validate(p) == 1
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sigattn_version() == S.VERSION
+    for code, text in S.STATUS.items():
+        assert lib.sigattn_status_string(code).decode() == text
+
+
+def _prob(**kw):
+    base = dict(B=2, H=3, Lmax=256, d=64, seqlens=[256, 100])
+    base.update(kw)
+    B, H, L, d, sl = base.pop("B"), base.pop("H"), base.pop("Lmax"), base.pop("d"), base.pop("seqlens")
+    return S.make_problem(B, H, L, d, sl, **base)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda p: setattr(p, "d", 96), 2),
+    (lambda p: setattr(p, "d", 32), 2),
+    (lambda p: setattr(p, "B", 257), 2),
+    (lambda p: setattr(p, "Lmax", 70000), 2),
+    (lambda p: setattr(p, "H", 0), 1),
+    (lambda p: setattr(p, "Lmax", 0), 1),
+    (lambda p: setattr(p, "dtype", 7), 2),
+    (lambda p: setattr(p, "out_dtype", 5), 2),
+    (lambda p: (setattr(p, "dtype", 1), setattr(p, "out_dtype", 0)), 2),
+    (lambda p: setattr(p, "fast_math", 2), 1),
+    (lambda p: setattr(p, "causal", 2), 1),
+    (lambda p: setattr(p, "stride_l", 32), 1),
+    (lambda p: setattr(p, "stride_l", 68), 3),      # 136-byte rows: not 16-byte aligned
+    (lambda p: setattr(p, "stride_h", 256 * 64 + 4), 3),
+    (lambda p: setattr(p, "scale", float("nan")), 1),
+    (lambda p: setattr(p, "scale", -1.0), 1),
+    (lambda p: setattr(p, "seqlens", None), 1),
+])
+def test_validation_codes(lib, mutate, code):
+    p, keep = _prob()
+    mutate(p)
+    assert S.validate(p) == code
+
+
+def test_validation_rejects_bad_lengths(lib):
+    p, keep = _prob(seqlens=[257, 10])
+    assert S.validate(p) == 1
+    p, keep = _prob(seqlens=[-1, 10])
+    assert S.validate(p) == 1
+
+
+def test_validation_gate_fields(lib):
+    p, keep = _prob(gate_ptr=4096, tau=0.05)
+    assert S.validate(p) == 0
+    p.gate_tau = -1.0
+    assert S.validate(p) == 1
+    p.gate_tau = 0.05
+    p.gate_eps = float("inf")
+    assert S.validate(p) == 1
+    p.gate_eps = 1e-8
+    p.gate = 4098          # not 4-byte aligned
+    assert S.validate(p) == 3
+    p.gate = 4096
+    p.gate_stride_b = 100  # shorter than Lmax
+    assert S.validate(p) == 1
+
+
+def test_entry_points_reject_before_launch(lib):
+    """Argument errors are returned synchronously and nothing is launched; these calls
+    pass fake device pointers, which would fault if anything were enqueued."""
+    p, keep = _prob()
+    ok = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    # null output
+    assert lib.sigattn_fwd(ctypes.byref(p), ok, ok, ok, None, None) == 1
+    # misaligned input
+    assert lib.sigattn_fwd(ctypes.byref(p), odd, ok, ok, ctypes.c_void_p(1 << 21), None) == 3
+    # output aliases an input
+    assert lib.sigattn_fwd(ctypes.byref(p), ok, ok, ok, ok, None) == 1
+    # dk and dv alias each other
+    two = ctypes.c_void_p(1 << 22)
+    assert lib.sigattn_bwd_dkdv(ctypes.byref(p), ok, ok, ok, ok, two, two, None) == 1
+    # unsupported head size, valid pointers otherwise
+    p.d = 80
+    assert lib.sigattn_bwd_dq(ctypes.byref(p), ok, ok, ok, ok, two, None) == 2
+    assert lib.sigattn_fwd(None, ok, ok, ok, two, None) == 1
+
+
+def test_empty_batch_is_a_noop(lib):
+    p, keep = S.make_problem(0, 2, 64, 64, [])
+    assert S.validate(p) == 0
+    # B = 0 enqueues nothing even with fake pointers
+    a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)
+    assert lib.sigattn_fwd(ctypes.byref(p), a, a, a, b, None) == 0
+    assert S.plan(p, 0)[0].shape == (0, 3)
+
+
+@pytest.mark.parametrize("pass_", [0, 1, 2])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_plan_covers_exactly_the_valid_tiles(lib, pass_, causal, d):
+    """Every tile holding a valid row is listed exactly once; fully padded tiles never
+    appear (block-sparse padding, section 4 of the sigmoid-attention paper)."""
+    seqlens = [1000, 0, 1, 4096, 257, 4096, 3000]
+    B, H, L = len(seqlens), 5, 4096
+    p, keep = S.make_problem(B, H, L, d, seqlens, causal=causal)
+    items, tile = S.plan(p, pass_)
+    got = sorted(map(tuple, items.tolist()))
+    want = sorted((b, h, t) for b, n in enumerate(seqlens) for h in range(H)
+                  for t in range((n + tile - 1) // tile))
+    assert got == want
+    assert len(set(got)) == len(got)
+
+
+def test_plan_orders_longest_first(lib):
+    """Bidirectional work is listed longest sequence first (before the XCD grouping,
+    which only permutes items within rounds of 8 chunks)."""
+    os.environ.pop("SIGATTN_XCD_CHUNK", None)
+    seqlens = [100, 4096, 2000]
+    p, keep = S.make_problem(3, 2, 4096, 64, seqlens)
+    items, tile = S.plan(p, 0)
+    # items of batch 1 (longest) come first in any prefix of whole rounds
+    first = items[: len(items) // 2, 0]
+    assert (first == 1).mean() > 0.5
+
+
+def test_plan_xcd_grouping_keeps_heads_together(lib):
+    """Blocks w, w+8, w+16, ... (one XCD under round-robin dispatch) get consecutive
+    items, so one head's tiles share an XCD."""
+    p, keep = S.make_problem(4, 12, 8192, 64, [8192] * 4)
+    items, tile = S.plan(p, 0)
+    xcd0 = items[0::8][:16]
+    assert len({(b, h) for b, h, t in xcd0.tolist()}) <= 2

@@ -424,3 +424,31 @@ def test_generator_is_seeded():
     b = W.generate(W.get("bidir_2k", B=2, H=1, L=64))
     for t in ("q", "k", "v", "do", "seqlens"):
         np.testing.assert_array_equal(a[t], b[t])
+
+
+def test_absolute_sums():
+    """The magnitude sums equal the outputs for non-negative inputs (then every term is
+    non-negative) and bound them otherwise."""
+    B, H, L, d = 2, 2, 12, 4
+    seqlens = [12, 7]
+    rng = np.random.default_rng(180)
+    q, k, v, do = (rng.standard_normal((B, H, L, d)) for _ in range(4))
+    g = rng.uniform(0.1, 1.0, (B, L))
+    pos = [np.abs(t) for t in (q, k, v, do)]
+    for kw in (dict(), dict(gate=g, causal=True)):
+        plain = O.backward(*pos, seqlens, **kw)
+        mag = O.backward(*pos, seqlens, absolute=True, **kw)
+        for a, b in zip(plain, mag):
+            np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+        signed = O.backward(q, k, v, do, seqlens, **kw)
+        mags = O.backward(q, k, v, do, seqlens, absolute=True, **kw)
+        for a, m in zip(signed, mags):
+            assert np.all(np.abs(a) <= m + 1e-12)
+        rows = np.arange(L)
+        for b in range(B):
+            for h in range(H):
+                np.testing.assert_allclose(O.dq_rows(q, k, v, do, seqlens, b, h, rows, absolute=True, **kw),
+                                           mags[0][b, h], rtol=1e-12, atol=1e-15)
+                dk, dv = O.dkdv_rows(q, k, v, do, seqlens, b, h, rows, absolute=True, **kw)
+                np.testing.assert_allclose(dk, mags[1][b, h], rtol=1e-11, atol=1e-15)
+                np.testing.assert_allclose(dv, mags[2][b, h], rtol=1e-12, atol=1e-15)
