@@ -46,14 +46,16 @@ def parse():
     ap.add_argument("--bf16-out", action="store_true", help="bf16 outputs instead of float")
     ap.add_argument("--also-fast", action="store_true",
                     help="also time fast math with bf16 outputs and report it beside the default")
-    ap.add_argument("--cpu-sample-heads", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="lower bound on the oracle time of the CPU baseline sample")
     return ap.parse_args()
 
 
-def cpu_baseline(data, w, heads):
+def cpu_baseline(data, w, min_seconds):
     """Time the oracle, as it stands, on a bounded sample of the same workload: full
-    forward + backward of `heads` (b, h) pairs taken from the batch entry with the median
-    length, on the host cores."""
+    forward + backward of whole heads of the batch entry with the median length, one
+    head after another until at least `min_seconds` have passed (or all heads of that
+    entry are done), on the host cores."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -63,26 +65,33 @@ def cpu_baseline(data, w, heads):
     sl = data["seqlens"]
     b = int(np.argsort(sl)[len(sl) // 2])
     n = int(sl[b])
-    H = min(heads, w.H)
-    q = data["q"][b:b + 1, :H].astype(np.float64)
-    k = data["k"][b:b + 1, :H].astype(np.float64)
-    v = data["v"][b:b + 1, :H].astype(np.float64)
-    do = data["do"][b:b + 1, :H].astype(np.float64)
     kw = dict(causal=w.causal)
-    t0 = time.perf_counter()
-    oracle.forward(q, k, v, [n], **kw)
-    t1 = time.perf_counter()
-    oracle.backward(q, k, v, do, [n], **kw)
-    t2 = time.perf_counter()
-    pairs = (n * (n + 1) // 2 if w.causal else n * n) * H
-    flops = 4.0 * w.d * pairs * 3.5   # forward + credited backward
+    t_fwd = t_bwd = 0.0
+    heads = 0
+    for h in range(w.H):
+        q = data["q"][b:b + 1, h:h + 1].astype(np.float64)
+        k = data["k"][b:b + 1, h:h + 1].astype(np.float64)
+        v = data["v"][b:b + 1, h:h + 1].astype(np.float64)
+        do = data["do"][b:b + 1, h:h + 1].astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, [n], **kw)
+        t1 = time.perf_counter()
+        oracle.backward(q, k, v, do, [n], **kw)
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_bwd += t2 - t1
+        heads += 1
+        if t_fwd + t_bwd >= min_seconds:
+            break
+    pairs = (n * (n + 1) // 2 if w.causal else n * n) * heads
+    flops = 4.0 * w.d * pairs * 3.5   # forward + credited backward (2.5x forward)
     return {
-        "value": flops / (t2 - t0) / 1e12,
+        "value": flops / (t_fwd + t_bwd) / 1e12,
         "unit": "TFLOPS",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle, forward+backward of {H} heads of batch entry {b} "
-                  f"(n={n}) of {w.name}; fwd {t1 - t0:.2f} s, bwd {t2 - t1:.2f} s",
+        "sample": f"fp64 numpy oracle, forward+backward of {heads} of the {w.H} heads of "
+                  f"batch entry {b} (n={n}) of {w.name}; fwd {t_fwd:.2f} s, bwd {t_bwd:.2f} s",
         "host": platform.processor() or platform.machine(),
         "host_cpus": os.cpu_count(),
     }
@@ -124,7 +133,7 @@ def main():
         res["fast_math_bf16_out"] = {k_: fast[k_] for k_ in ("value", "ms_per_step", "fwd_tflops",
                                                              "bwd_tflops", "fwd_pct_peak", "kernels")}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(data, w, args.cpu_sample_heads)
+        res["cpu_baseline"] = cpu_baseline(data, w, args.cpu_seconds)
     print(json.dumps(res))
 
 
