@@ -62,6 +62,7 @@ extern "C" {
 #define SIGATTN_VERSION 2
 #define SIGATTN_MAX_BATCH 256      /* B above this returns SIGATTN_ERR_UNSUPPORTED */
 #define SIGATTN_MAX_LEN 65535      /* Lmax above this returns SIGATTN_ERR_UNSUPPORTED */
+#define SIGATTN_MAX_ROW_STRIDE (1 << 22)  /* stride_l above this (elements): UNSUPPORTED */
 
 typedef enum {
   SIGATTN_OK = 0,
@@ -79,7 +80,7 @@ typedef struct sigattn_problem {
   int32_t dtype;                 /* sigattn_dtype of q, k, v, dO */
   int32_t out_dtype;             /* sigattn_dtype of o, dq, dk, dv (F32 when dtype is F32) */
   int32_t fast_math;             /* 0: hi+lo split operands (default); 1: single bf16 */
-  int64_t stride_b, stride_h, stride_l;  /* element strides, >= 0; stride_l >= d */
+  int64_t stride_b, stride_h, stride_l;  /* element strides, >= 0; d <= stride_l <= 2^22 */
   const int32_t* seqlens;        /* HOST [B]: valid length n_b, 0 <= n_b <= Lmax */
   int32_t causal;                /* 0: bidirectional; 1: key j allowed for query i iff j <= i */
   float scale;                   /* s; 0 selects 1/sqrt(d) */

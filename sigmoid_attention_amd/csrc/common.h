@@ -59,11 +59,21 @@ __device__ __forceinline__ void settle(V& x) {
 }
 
 // ---------------------------------------------------------------------------------
-// LDS tile layout: [rows][D] bf16, 16-byte chunks of each row XOR-swizzled by row & 7.
+// LDS tile layout: [rows][D] bf16; the 16-byte chunks of row r are permuted by
+// XOR with xsw<D>(r). The map is chosen (by exhaustive search over XOR maps of the row
+// bits) so that both read patterns below touch distinct banks in every pass, for LDS
+// widths of 32 or 64 four-byte banks: the row-operand read (32 consecutive rows, one
+// chunk) and the transposed column read (4 consecutive rows x 4 chunks).
 // ---------------------------------------------------------------------------------
 template <int D>
+__device__ __forceinline__ constexpr int xsw(int r) {
+  if (D == 64) return ((r & 3) << 1) ^ ((r >> 2) & 3);
+  return ((r & 1) << 2) ^ ((r & 2) * 5) ^ ((r >> 2) & 3);
+}
+
+template <int D>
 __device__ __forceinline__ uint32_t swz(int row, int col) {
-  return (uint32_t)(row * (D * 2) + ((((col >> 3) ^ (row & 7))) << 4) + ((col & 7) << 1));
+  return (uint32_t)(row * (D * 2) + (((col >> 3) ^ xsw<D>(row)) << 4) + ((col & 7) << 1));
 }
 
 __device__ __forceinline__ bf16x8 lds_read16(const char* base, uint32_t off) {
@@ -135,6 +145,85 @@ struct TileRegs {
     }
   }
 };
+
+// ---------------------------------------------------------------------------------
+// Direct global -> LDS staging (global_load_lds_dwordx4) of a [ROWS][D] bf16 tile in the
+// swizzled layout above, without passing through registers. One wave instruction moves
+// 64 x 16 bytes into one contiguous 1 KB block of LDS: lane L fills bytes [16L, 16L+16)
+// of the block. The swizzle is applied on the source side: the 16-byte slot `s` of tile
+// row `r` holds logical chunk s ^ xsw(r), so lane L loads that chunk. Rows past the
+// valid length are clamped to the last valid row (padded memory is never read; the
+// caller masks those keys). The data is in LDS once vmcnt reaches zero for the issuing
+// wave; a barrier then makes it visible to the workgroup.
+// ---------------------------------------------------------------------------------
+// One global_load_lds_dwordx4: 16 bytes per lane from base + voff into LDS at
+// lds_addr + 16 * lane. Written as inline assembly so that the compiler does not see an
+// LDS write in flight and does not make every later LDS read wait for it (it cannot tell
+// that the ring stage being filled is not the one being read). Completion is awaited
+// explicitly (vmcnt) before the barrier that publishes the stage. M0 is used by
+// nothing else in these kernels.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  // base and lds_addr are wave-uniform; make them scalar for the s-register operands
+  // (readfirstlane returns int: go through uint32_t so the low half is not sign-extended)
+  const uint64_t b = reinterpret_cast<uintptr_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t bs = (uint64_t)lo | ((uint64_t)hi << 32);
+  const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
+  // Wait states the hardware does not enforce: 5 between a VALU write of an SGPR (the
+  // readfirstlane above) and a memory instruction reading it, 1 between an SALU write
+  // of M0 and an LDS DMA that uses it.
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(bs), "s"(ls) : "memory");
+}
+
+template <int ROWS, int D, int NWAVES>
+struct DirectTile {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int BLOCKS = ROWS * CPR / 64;    // 1 KB blocks per tile
+  static constexpr int PER_WAVE = BLOCKS / NWAVES;
+  static_assert(BLOCKS % NWAVES == 0, "tile must split evenly over the waves");
+
+  // Per-lane constants: the tile row and the byte offset of the source chunk within it.
+  int row[PER_WAVE];
+  uint32_t col_bytes[PER_WAVE];
+  uint32_t lds_off[PER_WAVE];   // wave-uniform
+
+  __device__ __forceinline__ DirectTile() {
+    const int l = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int blk = i * NWAVES + w;
+      const int P = blk * 64 + l;
+      row[i] = P / CPR;
+      col_bytes[i] = (uint32_t)(((P % CPR) ^ xsw<D>(row[i])) * 16);
+      lds_off[i] = (uint32_t)blk * 1024u;
+    }
+  }
+
+  // Rows row_base .. row_base + ROWS - 1 of src (element row stride sl, which must keep
+  // ROWS * sl * 2 below 2^32), rows past last_row clamped to last_row.
+  __device__ __forceinline__ void load(char* lds_tile, const bf16* src, int64_t sl,
+                                       int row_base, int last_row) const {
+    const char* base = reinterpret_cast<const char*>(src + (int64_t)row_base * sl);
+    const int lim = last_row - row_base;
+    const uint32_t rb = (uint32_t)sl * 2u;
+    const uint32_t lds = (uint32_t)(uintptr_t)(SA_LDS char*)lds_tile;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int r = row[i] < lim ? row[i] : lim;
+      lds_dma16(base, (uint32_t)r * rb + col_bytes[i], lds + lds_off[i]);
+    }
+  }
+};
+
+// Wait until every vector-memory operation of this wave has completed (including direct
+// loads into LDS), then synchronise the workgroup.
+__device__ __forceinline__ void wait_vmem_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
 
 // ---------------------------------------------------------------------------------
 // Logistic function: sigma(x) = 1 / (1 + 2^t), t = -x * log2(e) = acc * c1 + c2 with

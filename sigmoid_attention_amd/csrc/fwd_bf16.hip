@@ -1,38 +1,70 @@
 // Forward pass of padded sigmoid attention on gfx950:
 //   O = sigma(s Q K^T + beta [+ log(g + eps)]) V'      (element-wise sigmoid, no row
 // statistics), "Better Models, Faster Training: Sigmoid Attention for single-cell
-// Foundation Models", section 3 equation; fused single pass that never materialises
-// the n x n matrix and never visits fully padded tiles (section 4).
+// Foundation Models", section 3 equation; one fused pass that never materialises the
+// n x n matrix and never visits fully padded tiles (section 4, block-sparse computation).
 //
 // One workgroup = 4 waves = one work item (b, h, query tile of BM rows). Each wave owns
-// QB blocks of 32 queries; its Q rows stay in registers as the B operand of
-// S^T = K Q^T. K and V tiles of 64 keys are double-buffered in LDS; the next tile's
-// global loads are in flight while the current one is computed. Per 32-key chunk:
-// S^T (MFMA) -> logistic in registers (exp2 + rcp, fp32) -> bf16 (hi + lo when SPLIT)
-// -> O^T += V^T P^T (MFMA; V^T read with transposed LDS loads). Only the last key tile (padding) and
-// diagonal tiles (causal) run the masked code path.
+// QB blocks of 32 queries held in registers as the B operand of S^T = K Q^T, so the fp32
+// result already has the register layout of the B operand of O^T += V^T P^T (P never goes
+// through LDS). K and V stream through a 3-stage LDS ring filled by direct global->LDS
+// loads two tiles ahead; one barrier per tile.
+//
+// Per 32-key chunk c a wave runs a software pipeline: the MFMAs of S(c+1) are issued
+// while the VALU evaluates the logistic function of S(c) (computed one chunk earlier), and
+// the P V MFMAs of each 8-key group follow the VALU work of that group, interleaved with
+// the next group's VALU work. At d = 64 the two transcendentals per pair (exp2, rcp; a
+// quarter of the FMA rate on gfx950) cost about as much as the two products, so keeping
+// both pipes busy at once is what sets the speed.
+//
+// Chunk modes (wave-uniform): interior chunks compute every pair; chunks that reach past
+// the valid length, or cross the wave's diagonal under the causal rule, zero the pairs
+// with key >= n or key > query. With a gate, a per-key table in LDS supplies the logit
+// offset (+inf for padded or dropped keys, which makes P exactly 0) and value factor.
+#include <type_traits>
+
 #include "common.h"
 
 namespace sa {
 
-template <int D, int QB>
+template <int D, int QB, int CPT, bool GATED>
 struct FwdTraits {
   static constexpr int kThreads = 256;
   static constexpr int kWaves = 4;
-  static constexpr int BM = kWaves * QB * 32;
-  static constexpr int BN = 64;
-  static constexpr int KS = D / 16;
-  static constexpr int DT = D / 32;
-  static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int STAGE = 2 * TILE_BYTES + 2 * BN * 4;   // K, V, per-key gate table
+  static constexpr int BM = kWaves * QB * 32;   // queries per work item
+  static constexpr int BN = 32 * CPT;           // keys per LDS tile
+  static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
+  static constexpr int DT = D / 32;             // 32-column blocks of O
+  static constexpr int TILE = BN * D * 2;       // bytes of one K (or V) tile
+  static constexpr int TAB = GATED ? 2 * BN * 4 : 0;   // per-key gate table
+  static constexpr int STAGE = 2 * TILE + TAB;  // K tile, V tile, gate table
+  static constexpr int NSTAGE = 3;
 };
 
-template <int D, int QB, bool CAUSAL, bool GATED, bool SPLIT>
-__global__ __launch_bounds__(256) void fwd_kernel(const KArgs a) {
-  using T = FwdTraits<D, QB>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+enum ChunkMode { kInterior = 0, kMasked = 1 };
+
+// Register row (within a 32-row MFMA result) of entry r, without the lane term 4*(l/32).
+__device__ __forceinline__ constexpr int arc(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Waves per SIMD the register budget is sized for: 3 when each wave holds one 32-query
+// block at d = 64, else 2.
+#ifndef SA_FWD64_QB
+#define SA_FWD64_QB 1
+#endif
+template <int D, int QB>
+struct FwdOcc {
+  static constexpr int value = 2;
+};
+
+template <int D, int QB, int CPT, bool CAUSAL, bool GATED, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<D, QB>::value, FwdOcc<D, QB>::value)))
+void fwd_kernel(const KArgs a) {
+  using T = FwdTraits<D, QB, CPT, GATED>;
+  using Tile = DirectTile<T::BN, D, T::kWaves>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
 
   const int l = lane_id(), w = wave_id();
+  const int lk = 4 * (l >> 5);
   const SplitSel sel;
   const Item it = decode_item(a, remap_block(blockIdx.x, a.nitems, a.xcd_chunk));
   const int n = it.n;
@@ -44,8 +76,42 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KArgs a) {
   const float* Gg = GATED ? a.gate + (int64_t)it.b * a.gsb : nullptr;
   const int64_t sl = a.sl;
   const int item_q0 = it.t * T::BM;
-  const int q0 = item_q0 + w * QB * 32;  // first query of this wave
+  const int q0 = item_q0 + w * QB * 32;   // first query of this wave
   const float c1 = a.c1, c2 = it.c2;
+
+  int kend = n;
+  if (CAUSAL) kend = (item_q0 + T::BM < n) ? item_q0 + T::BM : n;
+  const int nch = (kend + 31) / 32;                 // 32-key chunks of the item
+  const int ntiles = (nch + CPT - 1) / CPT;
+  // chunks this wave computes: none if all its queries are padding; under the causal
+  // rule only chunks holding a key <= its last valid query
+  int wch = q0 < n ? nch : 0;
+  if (CAUSAL && q0 < n) {
+    const int lastq = (q0 + QB * 32 < n ? q0 + QB * 32 : n) - 1;
+    wch = lastq / 32 + 1 < nch ? lastq / 32 + 1 : nch;
+  }
+
+  const Tile tile_loader;
+  auto issue_tile = [&](int t) {
+    char* st = smem + (t % T::NSTAGE) * T::STAGE;
+    tile_loader.load(st, Kg, sl, t * T::BN, last);
+    tile_loader.load(st + T::TILE, Vg, sl, t * T::BN, last);
+  };
+  // gate table of tile t: logit offset in the exp2 domain (+inf drops the key, which
+  // gives P = 0 exactly) and value factor, one entry per key, written by wave 0
+  auto fill_table = [&](int t) {
+    if (GATED && w == 0 && l < T::BN) {
+      float* tab = reinterpret_cast<float*>(smem + (t % T::NSTAGE) * T::STAGE + 2 * T::TILE);
+      const int key = t * T::BN + l;
+      const float g = Gg[key < last ? key : last];
+      const bool keep = key < n && !(key >= a.gate_sink && g < a.gate_tau);
+      tab[l] = keep ? c2 - __builtin_amdgcn_logf(g + a.gate_eps) : __builtin_inff();
+      tab[T::BN + l] = keep ? g : 0.0f;
+    }
+  };
+  issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+  fill_table(0);
 
   // Q rows as B operands: lane holds query q0 + 32qb + l%32, d = 16ks + 8(l/32) + 0..7.
   bf16x8 qop[QB][T::KS];
@@ -68,110 +134,159 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KArgs a) {
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) acc[qb][dt] = zero16();
 
-  int kend = n;
-  if (CAUSAL) kend = (item_q0 + T::BM < n) ? item_q0 + T::BM : n;
-  const int nkt = (kend + T::BN - 1) / T::BN;
+  wait_vmem_and_barrier();
 
-  TileRegs<T::BN, D, T::kThreads> kreg, vreg;
-  float greg = 0.0f;
-  auto load = [&](int kt) {
-    const int kb = kt * T::BN;
-    kreg.load(Kg, sl, kb, last);
-    vreg.load(Vg, sl, kb, last);
-    if (GATED && w == 0) {
-      const int key = kb + l;
-      greg = Gg[key < last ? key : last];
+  // S of unit 0 (chunk 0, query block 0)
+  f32x16 s_cur;
+  {
+    s_cur = zero16();
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+      s_cur = mfma(lds_row_operand<D>(smem, 0, 16 * ks), qop[0][ks], s_cur);
+  }
+
+  // The work of a chunk is split into units u = (chunk c, query block qb). Unit u
+  // evaluates the logistic function of S(u) while the MFMAs of S(u+1) run, then adds
+  // P(u) V(c) into O. S(u+1) uses the K rows of the same chunk for qb + 1 < QB, else
+  // those of chunk c + 1 (already in LDS: tiles t and t+1 are both visible in tile t).
+  //
+  // Logistic of the 4 entries r0..r0+3 of S(u) (one row group of the MFMA result),
+  // masked as the chunk mode requires, into p.
+  auto sig4 = [&](auto mode_tag, int qb, int r0, int kb, const float* tab, int krow,
+                  f32x16& p) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    f32x4 tc2, tg;
+    if (GATED) {
+      tc2 = *reinterpret_cast<const f32x4*>(tab + krow + 2 * r0 + lk);
+      tg = *reinterpret_cast<const f32x4*>(tab + T::BN + krow + 2 * r0 + lk);
+    }
+    // masked chunks keep key <= lim + kb + lk: key < n, and key <= query when causal
+    int lim = n - 1 - kb - lk;
+    if (CAUSAL) {
+      const int ld = q0 + 32 * qb + (l & 31) - kb - lk;
+      lim = ld < lim ? ld : lim;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + e;
+      float x = sigmoid_l2(s_cur[r], c1, GATED ? tc2[e] : c2);
+      if (GATED) x *= tg[e];
+      if (MODE == kMasked) x = arc(r) <= lim ? x : 0.0f;
+      p[r] = x;
     }
   };
-  auto store = [&](int kt) {
-    char* st = smem + (kt & 1) * T::STAGE;
-    kreg.store(st);
-    vreg.store(st + T::TILE_BYTES);
-    if (GATED && w == 0) {
-      // per-key logit offset in the exp2 domain (+inf drops the key) and value factor
-      const int key = kt * T::BN + l;
-      const bool keep = key < n && !(key >= a.gate_sink && greg < a.gate_tau);
-      float* tab = reinterpret_cast<float*>(st + 2 * T::TILE_BYTES);
-      tab[l] = keep ? c2 - __builtin_amdgcn_logf(greg + a.gate_eps) : __builtin_inff();
-      tab[T::BN + l] = greg;
+  auto to_bf16 = [&](const f32x16& p, int h, bf16x8& ph, bf16x8& pl) {
+    if (SPLIT) split8(p, 8 * h, ph, pl, sel);
+    else ph = pack8(p, 8 * h);
+  };
+
+  // P V of the second key half (h = 1) of a unit is deferred into the next unit, with
+  // its bf16 operands and V operands carried in registers (zero before the first unit,
+  // flushed after the last). Program order is fixed by scheduling barriers into steps
+  // that pair VALU work with MFMAs that do not depend on it; the K and V operand reads
+  // are issued first so that their latency hides behind the first VALU steps:
+  //   1: logistic of entries 0-3           | deferred P V (h = 1 of the previous unit)
+  //   2: entries 4-7, to bf16 (h = 0)      |   "          second half of d
+  //   3: entries 8-11                      | S(u+1), first half of the k-steps
+  //   4: entries 12-15, to bf16 (h = 1)    | S(u+1), second half; P V (h = 0)
+  bf16x8 dph = {}, dpl = {}, dvop[T::DT];
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt) dvop[dt] = bf16x8{};
+  int dqb = 0;
+  auto pv = [&](int qb, int dt, const bf16x8& vo, const bf16x8& hi, const bf16x8& lo) {
+    acc[qb][dt] = mfma(vo, hi, acc[qb][dt]);
+    if (SPLIT) acc[qb][dt] = mfma(vo, lo, acc[qb][dt]);
+  };
+
+  auto unit = [&](auto mode_tag, int qb, const char* Kn, int kn_row, int qb_next,
+                  const char* Vt, int v_row, const float* tab, int kb) {
+    bf16x8 kop[T::KS];
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lds_row_operand<D>(Kn, kn_row, 16 * ks);
+    bf16x8 vop0[T::DT], vop1[T::DT];
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) vop0[dt] = lds_col_operand<D>(Vt, v_row, 32 * dt);
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) vop1[dt] = lds_col_operand<D>(Vt, v_row + 16, 32 * dt);
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x16 p;
+    bf16x8 ph0, pl0, ph1, pl1;
+    f32x16 s_next = zero16();
+    // step 1
+    sig4(mode_tag, qb, 0, kb, tab, v_row, p);
+#pragma unroll
+    for (int dt = 0; dt < T::DT / 2; ++dt) pv(dqb, dt, dvop[dt], dph, dpl);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 2
+    sig4(mode_tag, qb, 4, kb, tab, v_row, p);
+    to_bf16(p, 0, ph0, pl0);
+#pragma unroll
+    for (int dt = T::DT / 2; dt < T::DT; ++dt) pv(dqb, dt, dvop[dt], dph, dpl);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 3
+    sig4(mode_tag, qb, 8, kb, tab, v_row, p);
+#pragma unroll
+    for (int ks = 0; ks < T::KS / 2; ++ks) s_next = mfma(kop[ks], qop[qb_next][ks], s_next);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 4
+    sig4(mode_tag, qb, 12, kb, tab, v_row, p);
+    to_bf16(p, 1, ph1, pl1);
+#pragma unroll
+    for (int ks = T::KS / 2; ks < T::KS; ++ks) s_next = mfma(kop[ks], qop[qb_next][ks], s_next);
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) pv(qb, dt, vop0[dt], ph0, pl0);
+    __builtin_amdgcn_sched_barrier(0);
+    s_cur = s_next;
+    dph = ph1;
+    dpl = pl1;
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) dvop[dt] = vop1[dt];
+    dqb = qb;
+  };
+
+  auto chunk = [&](auto mode_tag, const char* Kc, int kc_row, const char* Kn, int kn_row,
+                   const char* Vt, int v_row, const float* tab, int kb) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (qb + 1 < QB) unit(mode_tag, qb, Kc, kc_row, qb + 1, Vt, v_row, tab, kb);
+      else unit(mode_tag, qb, Kn, kn_row, 0, Vt, v_row, tab, kb);
     }
   };
 
-  load(0);
-  store(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) load(kt + 1);
-    __syncthreads();
-    const int kb = kt * T::BN;
-    // causal: skip tiles whose every key comes after every query of this wave
-    if (!CAUSAL || kb <= q0 + QB * 32 - 1) {
-      const char* Kt = smem + (kt & 1) * T::STAGE;
-      const char* Vt = Kt + T::TILE_BYTES;
-      const float* tab = reinterpret_cast<const float*>(Kt + 2 * T::TILE_BYTES);
-      const bool edge = kb + T::BN > n;
-      const bool diag = CAUSAL && (kb + T::BN - 1 > q0);
+  // Tiles before `tmask` hold only interior chunks for this wave; the rest run the
+  // masked body. Two loops without a mode branch inside; every wave passes the same
+  // number of barriers (one per tile).
+  int cfirst = n / 32;                                  // first chunk reaching past n
+  if (CAUSAL) cfirst = (q0 + 1) / 32 < cfirst ? (q0 + 1) / 32 : cfirst;
+  int tmask = cfirst / CPT;
+  tmask = tmask < ntiles ? tmask : ntiles;
+  if (q0 >= n) tmask = 0;                               // nothing to compute
 
+  auto tile_body = [&](auto mode_tag, int t) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    if (t > 0) wait_vmem_and_barrier();
+    if (t + 2 < ntiles) issue_tile(t + 2);
+    if (t + 1 < ntiles) fill_table(t + 1);
+    const char* cur = smem + (t % T::NSTAGE) * T::STAGE;
+    const char* nxt = smem + ((t + 1) % T::NSTAGE) * T::STAGE;
+    const float* tab = reinterpret_cast<const float*>(cur + 2 * T::TILE);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 kop[T::KS];
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lds_row_operand<D>(Kt, 32 * c, 16 * ks);
-
-        f32x4 gc2[4], gg[4];
-        if (GATED) {
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const int k4 = 32 * c + 8 * a4 + 4 * (l >> 5);
-            gc2[a4] = *reinterpret_cast<const f32x4*>(tab + k4);
-            gg[a4] = *reinterpret_cast<const f32x4*>(tab + T::BN + k4);
-          }
-        }
-
-        bf16x8 pb[QB][2], pl[QB][2];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          f32x16 s = zero16();
-#pragma unroll
-          for (int ks = 0; ks < T::KS; ++ks) s = mfma(kop[ks], qop[qb][ks], s);
-          f32x16 p;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if (GATED) p[r] = gg[r >> 2][r & 3] * sigmoid_l2(s[r], c1, gc2[r >> 2][r & 3]);
-            else p[r] = sigmoid_l2(s[r], c1, c2);
-          }
-          if (edge || diag) {
-            const int query = q0 + 32 * qb + (l & 31);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kb + 32 * c + acc_row(r, l);
-              const bool ok = key < n && (!CAUSAL || key <= query);
-              p[r] = ok ? p[r] : 0.0f;
-            }
-          }
-          if (SPLIT) {
-            split8(p, 0, pb[qb][0], pl[qb][0], sel);
-            split8(p, 8, pb[qb][1], pl[qb][1], sel);
-          } else {
-            pb[qb][0] = pack8(p, 0);
-            pb[qb][1] = pack8(p, 8);
-          }
-        }
-#pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-#pragma unroll
-          for (int ks2 = 0; ks2 < 2; ++ks2) {
-            const bf16x8 vop = lds_col_operand<D>(Vt, 32 * c + 16 * ks2, 32 * dt);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              acc[qb][dt] = mfma(vop, pb[qb][ks2], acc[qb][dt]);
-              if (SPLIT) acc[qb][dt] = mfma(vop, pl[qb][ks2], acc[qb][dt]);
-            }
-          }
-        }
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int c = t * CPT + cc;
+      if (MODE == kInterior || c < wch) {
+        const char* Kn = (cc + 1 < CPT) ? cur : nxt;
+        const int kn_row = ((cc + 1) % CPT) * 32;
+        chunk(mode_tag, cur, cc * 32, Kn, kn_row, cur + T::TILE, cc * 32, tab, c * 32);
       }
     }
-    if (kt + 1 < nkt) store(kt + 1);
-  }
+  };
+  for (int t = 0; t < tmask; ++t) tile_body(std::integral_constant<int, kInterior>{}, t);
+  for (int t = tmask; t < ntiles; ++t) tile_body(std::integral_constant<int, kMasked>{}, t);
+
+  // the deferred half of the last unit
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt) pv(dqb, dt, dvop[dt], dph, dpl);
 
   // epilogue: valid query rows only (rows >= n are zero-filled by a separate kernel)
 #pragma unroll
@@ -185,28 +300,28 @@ __global__ __launch_bounds__(256) void fwd_kernel(const KArgs a) {
   }
 }
 
-template <int D, int QB, bool C, bool G, bool SP>
+template <int D, int QB, int CPT, bool C, bool G, bool SP>
 static hipError_t launch_one(const KArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<D, QB, C, G, SP>), dim3(a.nitems), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP>), dim3(a.nitems), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, int QB>
+template <int D, int QB, int CPT>
 static hipError_t dispatch(const KArgs& a, bool c, bool g, bool sp, hipStream_t st) {
   if (c) {
-    if (g) return sp ? launch_one<D, QB, true, true, true>(a, st) : launch_one<D, QB, true, true, false>(a, st);
-    return sp ? launch_one<D, QB, true, false, true>(a, st) : launch_one<D, QB, true, false, false>(a, st);
+    if (g) return sp ? launch_one<D, QB, CPT, true, true, true>(a, st) : launch_one<D, QB, CPT, true, true, false>(a, st);
+    return sp ? launch_one<D, QB, CPT, true, false, true>(a, st) : launch_one<D, QB, CPT, true, false, false>(a, st);
   }
-  if (g) return sp ? launch_one<D, QB, false, true, true>(a, st) : launch_one<D, QB, false, true, false>(a, st);
-  return sp ? launch_one<D, QB, false, false, true>(a, st) : launch_one<D, QB, false, false, false>(a, st);
+  if (g) return sp ? launch_one<D, QB, CPT, false, true, true>(a, st) : launch_one<D, QB, CPT, false, true, false>(a, st);
+  return sp ? launch_one<D, QB, CPT, false, false, true>(a, st) : launch_one<D, QB, CPT, false, false, false>(a, st);
 }
 
-int fwd_tile_rows(int d) { return d == 64 ? FwdTraits<64, 2>::BM : FwdTraits<128, 1>::BM; }
+int fwd_tile_rows(int d) { return d == 64 ? FwdTraits<64, SA_FWD64_QB, 2, false>::BM : FwdTraits<128, 1, 1, false>::BM; }
 
 hipError_t launch_fwd_bf16(const KArgs& a, int d, bool causal, bool gated, bool split,
                            hipStream_t st) {
-  return d == 64 ? dispatch<64, 2>(a, causal, gated, split, st)
-                 : dispatch<128, 1>(a, causal, gated, split, st);
+  return d == 64 ? dispatch<64, SA_FWD64_QB, 2>(a, causal, gated, split, st)
+                 : dispatch<128, 1, 1>(a, causal, gated, split, st);
 }
 
 }  // namespace sa

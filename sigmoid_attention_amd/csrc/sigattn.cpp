@@ -59,6 +59,8 @@ sigattn_status validate_problem(const sigattn_problem* p) {
   if (p->dtype == SIGATTN_F32 && p->out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
   if (p->fast_math != 0 && p->fast_math != 1) return SIGATTN_ERR_INVALID_ARG;
   if (p->stride_b < 0 || p->stride_h < 0 || p->stride_l < p->d) return SIGATTN_ERR_INVALID_ARG;
+  // tile loads address up to 128 rows from a per-tile base with 32-bit byte offsets
+  if (p->stride_l > SIGATTN_MAX_ROW_STRIDE) return SIGATTN_ERR_UNSUPPORTED;
   if (p->B > 0 && !p->seqlens) return SIGATTN_ERR_INVALID_ARG;
   for (int b = 0; b < p->B; ++b)
     if (p->seqlens[b] < 0 || p->seqlens[b] > p->Lmax) return SIGATTN_ERR_INVALID_ARG;

@@ -74,6 +74,7 @@ def _prob(**kw):
     (lambda p: setattr(p, "stride_l", 32), 1),
     (lambda p: setattr(p, "stride_l", 68), 3),      # 136-byte rows: not 16-byte aligned
     (lambda p: setattr(p, "stride_h", 256 * 64 + 4), 3),
+    (lambda p: setattr(p, "stride_l", (1 << 22) + 8), 2),  # beyond the 32-bit tile offsets
     (lambda p: setattr(p, "scale", float("nan")), 1),
     (lambda p: setattr(p, "scale", -1.0), 1),
     (lambda p: setattr(p, "seqlens", None), 1),
