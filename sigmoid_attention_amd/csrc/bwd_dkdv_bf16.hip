@@ -6,36 +6,50 @@
 // Each key row belongs to exactly one workgroup, so results are accumulated in
 // registers and written once: no atomics, bitwise deterministic.
 //
-// One workgroup = 4 waves = one item (b, h, key tile of 128). Each wave keeps 32 key
-// rows of K and V in registers (B operands). Q and dO tiles of 64 queries are
-// double-buffered in LDS, the next tile's global loads in flight during the current.
-// Per 32-query chunk: S = Q K^T and dP = dO V^T (MFMA), P and dS in fp32 registers
-// (lane = key column), then dV^T += dO^T P and dK^T += Q^T dS (MFMA, with dO^T and
-// Q^T read by transposed LDS loads; P and dS as hi + lo when SPLIT).
+// One workgroup = 4 waves = one item (b, h, key tile of 128). Each wave keeps 32 key rows
+// of K and V in registers (B operands), so in S = Q K^T and dP = dO V^T every lane owns
+// one key column and the per-key gate terms are per-lane constants. Q and dO stream
+// through a 3-stage LDS ring filled by direct loads two tiles ahead. Per 32-query chunk
+// c (a unit): the logistic function of S(c) runs while the MFMAs of dP(c) and S(c+1)
+// execute; then dS, the bf16 operands, and dV^T += dO^T P, dK^T += Q^T dS (dO^T and Q^T
+// read with transposed LDS loads).
+#include <type_traits>
+
 #include "common.h"
 
 namespace sa {
 
-template <int D>
+template <int D, int CPT>
 struct DkvTraits {
   static constexpr int kThreads = 256;
   static constexpr int kWaves = 4;
-  static constexpr int BK = kWaves * 32;       // keys per item
-  static constexpr int BQ = 64;                // queries per LDS stage
+  static constexpr int BK = kWaves * 32;   // keys per item
+  static constexpr int BQ = 32 * CPT;      // queries per LDS tile
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
-  static constexpr int TILE_BYTES = BQ * D * 2;
-  static constexpr int STAGE = 2 * TILE_BYTES;   // Q, dO
+  static constexpr int TILE = BQ * D * 2;
+  static constexpr int STAGE = 2 * TILE;   // Q tile, dO tile
+  static constexpr int NSTAGE = 3;
 };
 
-template <int D, bool CAUSAL, bool GATED, bool SPLIT>
-__global__ __launch_bounds__(256) void dkdv_kernel(const KArgs a) {
-  using T = DkvTraits<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+enum DkvMode { kKvInterior = 0, kKvMasked = 1 };
+
+__device__ __forceinline__ constexpr int kv_arc(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// K, V, dK and dV of 32 keys take 96 registers per lane at d = 64 (two waves per SIMD)
+// and 192 at d = 128 (one wave per SIMD).
+template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
+void dkdv_kernel(const KArgs a) {
+  using T = DkvTraits<D, CPT>;
+  using Tile = DirectTile<T::BQ, D, T::kWaves>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
+  constexpr bool PIPE = D == 64;
 
   const int l = lane_id(), w = wave_id();
+  const int lk = 4 * (l >> 5);
   const SplitSel sel;
-  const Item it = decode_item(a, remap_block(blockIdx.x, a.nitems, a.xcd_chunk));
+  const Item it = block_item(a);
   const int n = it.n;
   const int last = n - 1;
   const int64_t hoff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
@@ -58,21 +72,38 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const KArgs a) {
     gmul = keep ? g : 0.0f;
   }
 
+  // query chunks of the item: all valid queries, or (causal) those from the item's
+  // first key on; this wave's first contributing chunk is c_lo
+  const int nch = (n + 31) / 32;
+  const int c_start = CAUSAL ? item_k0 / 32 : 0;
+  const int t0 = c_start / CPT;
+  const int ntiles = (nch + CPT - 1) / CPT;
+  int c_lo = CAUSAL ? k0 / 32 : 0;
+  if (k0 >= n) c_lo = nch;                  // all keys of this wave are padding
+
+  auto issue_tile = [&](int t) {
+    char* st = smem + (t % T::NSTAGE) * T::STAGE;
+    Tile::load(st, Qg, sl, t * T::BQ, last);
+    Tile::load(st + T::TILE, dOg, sl, t * T::BQ, last);
+  };
+  if (t0 < ntiles) issue_tile(t0);
+  if (t0 + 1 < ntiles) issue_tile(t0 + 1);
+
   // K and V rows as B operands: lane holds key mykey, d = 16ks + 8(l/32) + 0..7
-  bf16x8 kop[T::KS], vop[T::KS];
+  bf16x8 kreg[T::KS], vreg[T::KS];
   {
     const int row = mykey < last ? mykey : last;
     const bf16* kr = Kg + (int64_t)row * sl + 8 * (l >> 5);
     const bf16* vr = Vg + (int64_t)row * sl + 8 * (l >> 5);
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
-      kop[ks] = *reinterpret_cast<const bf16x8*>(kr + 16 * ks);
-      vop[ks] = *reinterpret_cast<const bf16x8*>(vr + 16 * ks);
+      kreg[ks] = *reinterpret_cast<const bf16x8*>(kr + 16 * ks);
+      vreg[ks] = *reinterpret_cast<const bf16x8*>(vr + 16 * ks);
     }
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
-      settle(kop[ks]);
-      settle(vop[ks]);
+      settle(kreg[ks]);
+      settle(vreg[ks]);
     }
   }
 
@@ -80,96 +111,162 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const KArgs a) {
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) { dk[dt] = zero16(); dv[dt] = zero16(); }
 
-  // query tiles: all valid queries, or those at or after the item's first key (causal)
-  const int qt0 = CAUSAL ? item_k0 / T::BQ : 0;
-  const int nqt = (n + T::BQ - 1) / T::BQ;
+  wait_vmem_and_barrier();
 
-  TileRegs<T::BQ, D, T::kThreads> qreg, doreg;
-  auto load = [&](int qt) {
-    qreg.load(Qg, sl, qt * T::BQ, last);
-    doreg.load(dOg, sl, qt * T::BQ, last);
-  };
-  auto store = [&](int qt) {
-    char* st = smem + (qt & 1) * T::STAGE;
-    qreg.store(st);
-    doreg.store(st + T::TILE_BYTES);
-  };
-
-  if (qt0 < nqt) {
-    load(qt0);
-    store(qt0);
+  // S of this wave's first chunk (its tile is one of the two loaded above)
+  f32x16 s_cur = zero16();
+  if (PIPE && c_lo < nch) {
+    const char* st = smem + ((c_lo / CPT) % T::NSTAGE) * T::STAGE;
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+      s_cur = mfma(lds_row_operand<D>(st, (c_lo % CPT) * 32, 16 * ks), kreg[ks], s_cur);
   }
-  for (int qt = qt0; qt < nqt; ++qt) {
-    if (qt + 1 < nqt) load(qt + 1);
-    __syncthreads();
-    const int qb0 = qt * T::BQ;
-    // causal: skip tiles whose every query comes before every key of this wave
-    if (!CAUSAL || qb0 + T::BQ - 1 >= k0) {
-      const char* Qt = smem + (qt & 1) * T::STAGE;
-      const char* dOt = Qt + T::TILE_BYTES;
-      const bool edge = qb0 + T::BQ > n;
-      const bool diag = CAUSAL && (qb0 < k0 + 31);
 
+  // logistic of the 16 entries of S(c), masked (query < n; key <= query if causal)
+  auto sig16 = [&](auto mode_tag, int qb0, f32x16& p) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    // keep query >= lo_q and query <= last: query = qb0 + lk + arc(r)
+    const int hi_lim = last - qb0 - lk;
+    const int lo_lim = mykey - qb0 - lk;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f32x16 s = zero16(), dp = zero16();
+    for (int r = 0; r < 16; ++r) {
+      float x = sigmoid_l2(s_cur[r], c1, c2);
+      if (MODE == kKvMasked) {
+        bool ok = kv_arc(r) <= hi_lim;
+        if (CAUSAL) ok = ok && kv_arc(r) >= lo_lim;
+        x = ok ? x : 0.0f;
+      }
+      p[r] = x;
+    }
+  };
+  auto to_bf16 = [&](const f32x16& v, int h, bf16x8& hi, bf16x8& lo) {
+    if (SPLIT) split8(v, 8 * h, hi, lo, sel);
+    else hi = pack8(v, 8 * h);
+  };
+  auto kv_mfma = [&](f32x16& acc, const bf16x8& op, const bf16x8& hi, const bf16x8& lo) {
+    acc = mfma(op, hi, acc);
+    if (SPLIT) acc = mfma(op, lo, acc);
+  };
+
+  // One unit (query chunk c), steps paired as VALU | MFMA:
+  //   1: logistic of S(c)                     | dP(c), S(c+1)
+  //   2: dS = dP P (1 - P), bf16 of h = 0     | -
+  //   3: bf16 of h = 1                        | dV, dK for the first query half of c
+  //   4: -                                    | dV, dK for the second query half
+  // (the MFMA-only step overlaps the VALU steps of the other wave on the SIMD)
+  auto unit = [&](auto mode_tag, const char* Qc, const char* dOc, int qrow, const char* Qn,
+                  int qn_row, int qb0) {
+    bf16x8 dor[T::KS], qnr[T::KS];
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-          const bf16x8 qa = lds_row_operand<D>(Qt, 32 * c, 16 * ks);
-          const bf16x8 da = lds_row_operand<D>(dOt, 32 * c, 16 * ks);
-          s = mfma(qa, kop[ks], s);
-          dp = mfma(da, vop[ks], dp);
-        }
-        f32x16 p, ds;
+    for (int ks = 0; ks < T::KS; ++ks) dor[ks] = lds_row_operand<D>(dOc, qrow, 16 * ks);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = sigmoid_l2(s[r], c1, c2);
-          ds[r] = dp[r] * __builtin_fmaf(-p[r], p[r], p[r]);
-        }
-        if (edge || diag) {
+    for (int ks = 0; ks < T::KS; ++ks) qnr[ks] = lds_row_operand<D>(Qn, qn_row, 16 * ks);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1
+    f32x16 p, dp = zero16(), s_next = zero16();
+    sig16(mode_tag, qb0, p);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int query = qb0 + 32 * c + acc_row(r, l);
-            const bool ok = query < n && (!CAUSAL || mykey <= query);
-            p[r] = ok ? p[r] : 0.0f;
-            ds[r] = ok ? ds[r] : 0.0f;
-          }
-        }
-        bf16x8 pb0, pb1, db0, db1, pl0, pl1, dl0, dl1;
-        if (SPLIT) {
-          split8(p, 0, pb0, pl0, sel);
-          split8(p, 8, pb1, pl1, sel);
-          split8(ds, 0, db0, dl0, sel);
-          split8(ds, 8, db1, dl1, sel);
+    for (int ks = 0; ks < T::KS; ++ks) dp = mfma(dor[ks], vreg[ks], dp);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) s_next = mfma(qnr[ks], kreg[ks], s_next);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 2
+    bf16x8 do0[T::DT], qc0[T::DT];
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) {
+      do0[dt] = lds_col_operand<D>(dOc, qrow, 32 * dt);
+      qc0[dt] = lds_col_operand<D>(Qc, qrow, 32 * dt);
+    }
+    f32x16 ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = dp[r] * __builtin_fmaf(-p[r], p[r], p[r]);
+    bf16x8 ph0, pl0, dh0, dl0, ph1, pl1, dh1, dl1;
+    to_bf16(p, 0, ph0, pl0);
+    to_bf16(ds, 0, dh0, dl0);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 3
+    bf16x8 do1[T::DT], qc1[T::DT];
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) {
+      do1[dt] = lds_col_operand<D>(dOc, qrow + 16, 32 * dt);
+      qc1[dt] = lds_col_operand<D>(Qc, qrow + 16, 32 * dt);
+    }
+    to_bf16(p, 1, ph1, pl1);
+    to_bf16(ds, 1, dh1, dl1);
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) {
+      kv_mfma(dv[dt], do0[dt], ph0, pl0);
+      kv_mfma(dk[dt], qc0[dt], dh0, dl0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // step 4
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) {
+      kv_mfma(dv[dt], do1[dt], ph1, pl1);
+      kv_mfma(dk[dt], qc1[dt], dh1, dl1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s_cur = s_next;
+  };
+
+  // d = 128: no cross-unit pipelining (four times the operand registers)
+  auto unit_flat = [&](auto mode_tag, const char* Qc, const char* dOc, int qrow, int qb0) {
+    f32x16 dp = zero16();
+    s_cur = zero16();
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      s_cur = mfma(lds_row_operand<D>(Qc, qrow, 16 * ks), kreg[ks], s_cur);
+      dp = mfma(lds_row_operand<D>(dOc, qrow, 16 * ks), vreg[ks], dp);
+    }
+    f32x16 p, ds;
+    sig16(mode_tag, qb0, p);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = dp[r] * __builtin_fmaf(-p[r], p[r], p[r]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 ph, pl, dh, dl;
+      to_bf16(p, h, ph, pl);
+      to_bf16(ds, h, dh, dl);
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        kv_mfma(dv[dt], lds_col_operand<D>(dOc, qrow + 16 * h, 32 * dt), ph, pl);
+        kv_mfma(dk[dt], lds_col_operand<D>(Qc, qrow + 16 * h, 32 * dt), dh, dl);
+      }
+    }
+  };
+
+  // Tile loops: [t0, tm1) masked (the causal diagonal chunk), [tm1, tm2) interior,
+  // [tm2, ntiles) masked (the chunk holding the last valid query when n % 32 != 0).
+  // Every wave passes one barrier per tile.
+  int tm1 = CAUSAL ? c_lo / CPT + 1 : t0;
+  int tm2 = (n % 32 != 0) ? (nch - 1) / CPT : ntiles;
+  if (c_lo >= nch) { tm1 = ntiles; tm2 = ntiles; }
+  tm1 = tm1 < ntiles ? tm1 : ntiles;
+  tm2 = tm2 > tm1 ? tm2 : tm1;
+  tm2 = tm2 < ntiles ? tm2 : ntiles;
+
+  auto tile_body = [&](auto mode_tag, int t) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    if (t > t0) wait_vmem_and_barrier();
+    if (t + 2 < ntiles) issue_tile(t + 2);
+    const char* cur = smem + (t % T::NSTAGE) * T::STAGE;
+    const char* nxt = smem + ((t + 1) % T::NSTAGE) * T::STAGE;
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int c = t * CPT + cc;
+      if (MODE == kKvInterior || (c >= c_lo && c < nch)) {
+        if (PIPE) {
+          const char* Qn = (cc + 1 < CPT) ? cur : nxt;
+          unit(mode_tag, cur, cur + T::TILE, cc * 32, Qn, ((cc + 1) % CPT) * 32, c * 32);
         } else {
-          pb0 = pack8(p, 0);
-          pb1 = pack8(p, 8);
-          db0 = pack8(ds, 0);
-          db1 = pack8(ds, 8);
-        }
-#pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-          const bf16x8 doT0 = lds_col_operand<D>(dOt, 32 * c, 32 * dt);
-          const bf16x8 doT1 = lds_col_operand<D>(dOt, 32 * c + 16, 32 * dt);
-          dv[dt] = mfma(doT0, pb0, dv[dt]);
-          dv[dt] = mfma(doT1, pb1, dv[dt]);
-          if (SPLIT) {
-            dv[dt] = mfma(doT0, pl0, dv[dt]);
-            dv[dt] = mfma(doT1, pl1, dv[dt]);
-          }
-          const bf16x8 qT0 = lds_col_operand<D>(Qt, 32 * c, 32 * dt);
-          const bf16x8 qT1 = lds_col_operand<D>(Qt, 32 * c + 16, 32 * dt);
-          dk[dt] = mfma(qT0, db0, dk[dt]);
-          dk[dt] = mfma(qT1, db1, dk[dt]);
-          if (SPLIT) {
-            dk[dt] = mfma(qT0, dl0, dk[dt]);
-            dk[dt] = mfma(qT1, dl1, dk[dt]);
-          }
+          unit_flat(mode_tag, cur, cur + T::TILE, cc * 32, c * 32);
         }
       }
     }
-    if (qt + 1 < nqt) store(qt + 1);
-  }
+  };
+  for (int t = t0; t < tm1; ++t) tile_body(std::integral_constant<int, kKvMasked>{}, t);
+  for (int t = tm1; t < tm2; ++t) tile_body(std::integral_constant<int, kKvInterior>{}, t);
+  for (int t = tm2; t < ntiles; ++t) tile_body(std::integral_constant<int, kKvMasked>{}, t);
 
   if (mykey < n) {
     const int64_t roff = hoff + (int64_t)mykey * sl;
@@ -181,27 +278,27 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const KArgs a) {
   }
 }
 
-template <int D, bool C, bool G, bool SP>
+template <int D, int CPT, bool C, bool G, bool SP>
 static hipError_t launch_one(const KArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((dkdv_kernel<D, C, G, SP>), dim3(a.nitems), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((dkdv_kernel<D, CPT, C, G, SP>), dim3(a.nitems), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int CPT>
 static hipError_t dispatch(const KArgs& a, bool c, bool g, bool sp, hipStream_t st) {
   if (c) {
-    if (g) return sp ? launch_one<D, true, true, true>(a, st) : launch_one<D, true, true, false>(a, st);
-    return sp ? launch_one<D, true, false, true>(a, st) : launch_one<D, true, false, false>(a, st);
+    if (g) return sp ? launch_one<D, CPT, true, true, true>(a, st) : launch_one<D, CPT, true, true, false>(a, st);
+    return sp ? launch_one<D, CPT, true, false, true>(a, st) : launch_one<D, CPT, true, false, false>(a, st);
   }
-  if (g) return sp ? launch_one<D, false, true, true>(a, st) : launch_one<D, false, true, false>(a, st);
-  return sp ? launch_one<D, false, false, true>(a, st) : launch_one<D, false, false, false>(a, st);
+  if (g) return sp ? launch_one<D, CPT, false, true, true>(a, st) : launch_one<D, CPT, false, true, false>(a, st);
+  return sp ? launch_one<D, CPT, false, false, true>(a, st) : launch_one<D, CPT, false, false, false>(a, st);
 }
 
-int dkdv_tile_rows(int d) { return d == 64 ? DkvTraits<64>::BK : DkvTraits<128>::BK; }
+int dkdv_tile_rows(int d) { return d == 64 ? DkvTraits<64, 2>::BK : DkvTraits<128, 1>::BK; }
 
 hipError_t launch_dkdv_bf16(const KArgs& a, int d, bool causal, bool gated, bool split,
                             hipStream_t st) {
-  return d == 64 ? dispatch<64>(a, causal, gated, split, st) : dispatch<128>(a, causal, gated, split, st);
+  return d == 64 ? dispatch<64, 2>(a, causal, gated, split, st) : dispatch<128, 1>(a, causal, gated, split, st);
 }
 
 }  // namespace sa

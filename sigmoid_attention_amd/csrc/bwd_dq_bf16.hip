@@ -5,36 +5,48 @@
 // decomposition: one kernel for dQ, one for dK/dV, no atomics). The factor
 // P(1 - P) is the diagonal of the sigmoid Jacobian (appendix A.1.2).
 //
-// One workgroup = 4 waves = one item (b, h, query tile). Each wave keeps its Q and dO
-// rows in registers (B operands). K and V tiles are double-buffered in LDS, the next
-// tile's global loads in flight during the current tile. Per 32-key chunk:
-// S^T = K Q^T and dP^T = V dO^T (MFMA), then P, dS in fp32 registers, then
-// dQ^T += K^T dS^T (MFMA with K^T read by transposed LDS loads; dS as hi + lo when
-// SPLIT).
+// One workgroup = 4 waves = one item (b, h, query tile of 128). Each wave keeps its 32
+// Q and dO rows in registers as B operands. K and V stream through the same 3-stage LDS
+// ring as the forward (direct loads two tiles ahead, one barrier per tile). Per 32-key
+// chunk c (a unit): S^T = K Q^T and dP^T = V dO^T (MFMA) of chunk c+1 are computed while
+// the VALU turns S(c), dP(c) into dS(c) (fp32, then bf16 hi + lo when SPLIT), and
+// dQ^T += K^T dS^T (K^T read with transposed LDS loads) for the first key half of c;
+// the second key half is deferred into the next unit.
+#include <type_traits>
+
 #include "common.h"
 
 namespace sa {
 
-template <int D, int QB>
+template <int D, int CPT, bool GATED>
 struct DqTraits {
   static constexpr int kThreads = 256;
   static constexpr int kWaves = 4;
-  static constexpr int BM = kWaves * QB * 32;
-  static constexpr int BN = 64;
+  static constexpr int BM = kWaves * 32;        // queries per work item
+  static constexpr int BN = 32 * CPT;           // keys per LDS tile
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
-  static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int STAGE = 2 * TILE_BYTES + 2 * BN * 4;   // K, V, per-key gate table
+  static constexpr int TILE = BN * D * 2;
+  static constexpr int TAB = GATED ? 2 * BN * 4 : 0;
+  static constexpr int STAGE = 2 * TILE + TAB;  // K tile, V tile, gate table
+  static constexpr int NSTAGE = 3;
 };
 
-template <int D, int QB, bool CAUSAL, bool GATED, bool SPLIT>
-__global__ __launch_bounds__(256) void dq_kernel(const KArgs a) {
-  using T = DqTraits<D, QB>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+enum DqMode { kDqInterior = 0, kDqMasked = 1 };
+
+__device__ __forceinline__ constexpr int dq_arc(int r) { return 8 * (r >> 2) + (r & 3); }
+
+template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dq_kernel(const KArgs a) {
+  using T = DqTraits<D, CPT, GATED>;
+  using Tile = DirectTile<T::BN, D, T::kWaves>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
 
   const int l = lane_id(), w = wave_id();
+  const int lk = 4 * (l >> 5);
   const SplitSel sel;
-  const Item it = decode_item(a, remap_block(blockIdx.x, a.nitems, a.xcd_chunk));
+  const Item it = block_item(a);
   const int n = it.n;
   const int last = n - 1;
   const int64_t hoff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
@@ -45,176 +57,241 @@ __global__ __launch_bounds__(256) void dq_kernel(const KArgs a) {
   const float* Gg = GATED ? a.gate + (int64_t)it.b * a.gsb : nullptr;
   const int64_t sl = a.sl;
   const int item_q0 = it.t * T::BM;
-  const int q0 = item_q0 + w * QB * 32;
+  const int q0 = item_q0 + w * 32;
   const float c1 = a.c1, c2 = it.c2;
 
-  bf16x8 qop[QB][T::KS], doop[QB][T::KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    int row = q0 + 32 * qb + (l & 31);
+  int kend = n;
+  if (CAUSAL) kend = (item_q0 + T::BM < n) ? item_q0 + T::BM : n;
+  const int nch = (kend + 31) / 32;
+  const int ntiles = (nch + CPT - 1) / CPT;
+  int wch = q0 < n ? nch : 0;
+  if (CAUSAL && q0 < n) {
+    const int lastq = (q0 + 32 < n ? q0 + 32 : n) - 1;
+    wch = lastq / 32 + 1 < nch ? lastq / 32 + 1 : nch;
+  }
+
+  auto issue_tile = [&](int t) {
+    char* st = smem + (t % T::NSTAGE) * T::STAGE;
+    Tile::load(st, Kg, sl, t * T::BN, last);
+    Tile::load(st + T::TILE, Vg, sl, t * T::BN, last);
+  };
+  auto fill_table = [&](int t) {
+    if (GATED && w == 0 && l < T::BN) {
+      float* tab = reinterpret_cast<float*>(smem + (t % T::NSTAGE) * T::STAGE + 2 * T::TILE);
+      const int key = t * T::BN + l;
+      const float g = Gg[key < last ? key : last];
+      const bool keep = key < n && !(key >= a.gate_sink && g < a.gate_tau);
+      tab[l] = keep ? c2 - __builtin_amdgcn_logf(g + a.gate_eps) : __builtin_inff();
+      tab[T::BN + l] = keep ? g : 0.0f;
+    }
+  };
+  issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+  fill_table(0);
+
+  bf16x8 qop[T::KS], doop[T::KS];
+  {
+    int row = q0 + (l & 31);
     row = row < last ? row : last;
     const bf16* qr = Qg + (int64_t)row * sl + 8 * (l >> 5);
     const bf16* dr = dOg + (int64_t)row * sl + 8 * (l >> 5);
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
-      qop[qb][ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
-      doop[qb][ks] = *reinterpret_cast<const bf16x8*>(dr + 16 * ks);
+      qop[ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+      doop[ks] = *reinterpret_cast<const bf16x8*>(dr + 16 * ks);
     }
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
-      settle(qop[qb][ks]);
-      settle(doop[qb][ks]);
+      settle(qop[ks]);
+      settle(doop[ks]);
     }
-
-  f32x16 acc[QB][T::DT];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) acc[qb][dt] = zero16();
-
-  int kend = n;
-  if (CAUSAL) kend = (item_q0 + T::BM < n) ? item_q0 + T::BM : n;
-  const int nkt = (kend + T::BN - 1) / T::BN;
-
-  TileRegs<T::BN, D, T::kThreads> kreg, vreg;
-  float greg = 0.0f;
-  auto load = [&](int kt) {
-    const int kb = kt * T::BN;
-    kreg.load(Kg, sl, kb, last);
-    vreg.load(Vg, sl, kb, last);
-    if (GATED && w == 0) {
-      const int key = kb + l;
-      greg = Gg[key < last ? key : last];
-    }
-  };
-  auto store = [&](int kt) {
-    char* st = smem + (kt & 1) * T::STAGE;
-    kreg.store(st);
-    vreg.store(st + T::TILE_BYTES);
-    if (GATED && w == 0) {
-      const int key = kt * T::BN + l;
-      const bool keep = key < n && !(key >= a.gate_sink && greg < a.gate_tau);
-      float* tab = reinterpret_cast<float*>(st + 2 * T::TILE_BYTES);
-      tab[l] = keep ? c2 - __builtin_amdgcn_logf(greg + a.gate_eps) : __builtin_inff();
-      tab[T::BN + l] = greg;
-    }
-  };
-
-  load(0);
-  store(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) load(kt + 1);
-    __syncthreads();
-    const int kb = kt * T::BN;
-    if (!CAUSAL || kb <= q0 + QB * 32 - 1) {
-      const char* Kt = smem + (kt & 1) * T::STAGE;
-      const char* Vt = Kt + T::TILE_BYTES;
-      const float* tab = reinterpret_cast<const float*>(Kt + 2 * T::TILE_BYTES);
-      const bool edge = kb + T::BN > n;
-      const bool diag = CAUSAL && (kb + T::BN - 1 > q0);
-
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 kop[T::KS], vop[T::KS];
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-          kop[ks] = lds_row_operand<D>(Kt, 32 * c, 16 * ks);
-          vop[ks] = lds_row_operand<D>(Vt, 32 * c, 16 * ks);
-        }
-        f32x4 gc2[4], gg[4];
-        if (GATED) {
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const int k4 = 32 * c + 8 * a4 + 4 * (l >> 5);
-            gc2[a4] = *reinterpret_cast<const f32x4*>(tab + k4);
-            gg[a4] = *reinterpret_cast<const f32x4*>(tab + T::BN + k4);
-          }
-        }
-        bf16x8 dsb[QB][2], dsl[QB][2];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-          for (int ks = 0; ks < T::KS; ++ks) {
-            s = mfma(kop[ks], qop[qb][ks], s);
-            dp = mfma(vop[ks], doop[qb][ks], dp);
-          }
-          f32x16 ds;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = sigmoid_l2(s[r], c1, GATED ? gc2[r >> 2][r & 3] : c2);
-            const float sp = __builtin_fmaf(-p, p, p);   // p (1 - p)
-            ds[r] = dp[r] * (GATED ? sp * gg[r >> 2][r & 3] : sp);
-          }
-          if (edge || diag) {
-            const int query = q0 + 32 * qb + (l & 31);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kb + 32 * c + acc_row(r, l);
-              const bool ok = key < n && (!CAUSAL || key <= query);
-              ds[r] = ok ? ds[r] : 0.0f;
-            }
-          }
-          if (SPLIT) {
-            split8(ds, 0, dsb[qb][0], dsl[qb][0], sel);
-            split8(ds, 8, dsb[qb][1], dsl[qb][1], sel);
-          } else {
-            dsb[qb][0] = pack8(ds, 0);
-            dsb[qb][1] = pack8(ds, 8);
-          }
-        }
-#pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-#pragma unroll
-          for (int ks2 = 0; ks2 < 2; ++ks2) {
-            const bf16x8 kT = lds_col_operand<D>(Kt, 32 * c + 16 * ks2, 32 * dt);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              acc[qb][dt] = mfma(kT, dsb[qb][ks2], acc[qb][dt]);
-              if (SPLIT) acc[qb][dt] = mfma(kT, dsl[qb][ks2], acc[qb][dt]);
-            }
-          }
-        }
-      }
-    }
-    if (kt + 1 < nkt) store(kt + 1);
   }
 
+  f32x16 acc[T::DT];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int query = q0 + 32 * qb + (l & 31);
-    if (query < n) {
+  for (int dt = 0; dt < T::DT; ++dt) acc[dt] = zero16();
+
+  wait_vmem_and_barrier();
+
+  // S^T and dP^T of chunk 0
+  f32x16 s_cur = zero16(), dp_cur = zero16();
+#pragma unroll
+  for (int ks = 0; ks < (D == 64 ? T::KS : 0); ++ks) {
+    s_cur = mfma(lds_row_operand<D>(smem, 0, 16 * ks), qop[ks], s_cur);
+    dp_cur = mfma(lds_row_operand<D>(smem + T::TILE, 0, 16 * ks), doop[ks], dp_cur);
+  }
+
+  // dS of the 4 entries r0..r0+3 (fp32) into ds
+  auto ds4 = [&](auto mode_tag, int r0, int kb, const float* tab, int krow, f32x16& ds) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    f32x4 tc2, tg;
+    if (GATED) {
+      tc2 = *reinterpret_cast<const f32x4*>(tab + krow + 2 * r0 + lk);
+      tg = *reinterpret_cast<const f32x4*>(tab + T::BN + krow + 2 * r0 + lk);
+    }
+    int lim = n - 1 - kb - lk;
+    if (CAUSAL) {
+      const int ld = q0 + (l & 31) - kb - lk;
+      lim = ld < lim ? ld : lim;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + e;
+      const float p = sigmoid_l2(s_cur[r], c1, GATED ? tc2[e] : c2);
+      const float sp = __builtin_fmaf(-p, p, p);   // p (1 - p)
+      float x = dp_cur[r] * (GATED ? sp * tg[e] : sp);
+      if (MODE == kDqMasked) x = dq_arc(r) <= lim ? x : 0.0f;
+      ds[r] = x;
+    }
+  };
+  auto to_bf16 = [&](const f32x16& v, int h, bf16x8& hi, bf16x8& lo) {
+    if (SPLIT) split8(v, 8 * h, hi, lo, sel);
+    else hi = pack8(v, 8 * h);
+  };
+
+  bf16x8 dsh = {}, dsl = {}, dkc[T::DT];
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt) dkc[dt] = bf16x8{};
+  auto dq_mfma = [&](int dt, const bf16x8& kc, const bf16x8& hi, const bf16x8& lo) {
+    acc[dt] = mfma(kc, hi, acc[dt]);
+    if (SPLIT) acc[dt] = mfma(kc, lo, acc[dt]);
+  };
+
+  // One unit (chunk c): steps pair VALU work with MFMAs that do not depend on it.
+  //   1: dS entries 0-3              | deferred dQ (second key half of chunk c-1)
+  //   2: entries 4-7, to bf16 (h=0)  | S^T of chunk c+1
+  //   3: entries 8-11                | dP^T of chunk c+1
+  //   4: entries 12-15, to bf16 (h=1)| dQ for the first key half of chunk c
+  auto unit = [&](auto mode_tag, const char* Kc, int krow, const char* Kn, int kn_row,
+                  const char* Vn, const float* tab, int kb) {
+    bf16x8 kop[T::KS], vop[T::KS], kc0[T::DT], kc1[T::DT];
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lds_row_operand<D>(Kn, kn_row, 16 * ks);
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) kc0[dt] = lds_col_operand<D>(Kc, krow, 32 * dt);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) vop[ks] = lds_row_operand<D>(Vn, kn_row, 16 * ks);
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) kc1[dt] = lds_col_operand<D>(Kc, krow + 16, 32 * dt);
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x16 ds;
+    bf16x8 h0, l0, h1, l1;
+    f32x16 s_next = zero16(), dp_next = zero16();
+    // step 1
+    ds4(mode_tag, 0, kb, tab, krow, ds);
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) dq_mfma(dt, dkc[dt], dsh, dsl);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 2
+    ds4(mode_tag, 4, kb, tab, krow, ds);
+    to_bf16(ds, 0, h0, l0);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) s_next = mfma(kop[ks], qop[ks], s_next);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 3
+    ds4(mode_tag, 8, kb, tab, krow, ds);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) dp_next = mfma(vop[ks], doop[ks], dp_next);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 4
+    ds4(mode_tag, 12, kb, tab, krow, ds);
+    to_bf16(ds, 1, h1, l1);
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) dq_mfma(dt, kc0[dt], h0, l0);
+    __builtin_amdgcn_sched_barrier(0);
+    s_cur = s_next;
+    dp_cur = dp_next;
+    dsh = h1;
+    dsl = l1;
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) dkc[dt] = kc1[dt];
+  };
+
+  // d = 128 (four times the operand registers): no cross-unit pipelining. S^T and dP^T of
+  // chunk c are formed at the start of its unit, the K^T operands read per key half.
+  auto unit_flat = [&](auto mode_tag, const char* Kc, int krow, const float* tab, int kb) {
+    s_cur = zero16();
+    dp_cur = zero16();
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      s_cur = mfma(lds_row_operand<D>(Kc, krow, 16 * ks), qop[ks], s_cur);
+      dp_cur = mfma(lds_row_operand<D>(Kc + T::TILE, krow, 16 * ks), doop[ks], dp_cur);
+    }
+    f32x16 ds;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ds4(mode_tag, 8 * h, kb, tab, krow, ds);
+      ds4(mode_tag, 8 * h + 4, kb, tab, krow, ds);
+      bf16x8 hi, lo;
+      to_bf16(ds, h, hi, lo);
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
-        store_row(a.out0, hoff + (int64_t)query * sl, a.out_f32, acc[qb][dt], 32 * dt, a.scale);
+        dq_mfma(dt, lds_col_operand<D>(Kc, krow + 16 * h, 32 * dt), hi, lo);
     }
+  };
+  constexpr bool PIPE = D == 64;
+
+  int cfirst = n / 32;
+  if (CAUSAL) cfirst = (q0 + 1) / 32 < cfirst ? (q0 + 1) / 32 : cfirst;
+  int tmask = cfirst / CPT;
+  tmask = tmask < ntiles ? tmask : ntiles;
+  if (q0 >= n) tmask = 0;
+
+  auto tile_body = [&](auto mode_tag, int t) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    if (t > 0) wait_vmem_and_barrier();
+    if (t + 2 < ntiles) issue_tile(t + 2);
+    if (t + 1 < ntiles) fill_table(t + 1);
+    const char* cur = smem + (t % T::NSTAGE) * T::STAGE;
+    const char* nxt = smem + ((t + 1) % T::NSTAGE) * T::STAGE;
+    const float* tab = reinterpret_cast<const float*>(cur + 2 * T::TILE);
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int c = t * CPT + cc;
+      if (MODE == kDqInterior || c < wch) {
+        const char* Kn = (cc + 1 < CPT) ? cur : nxt;
+        const int kn_row = ((cc + 1) % CPT) * 32;
+        if (PIPE) unit(mode_tag, cur, cc * 32, Kn, kn_row, Kn + T::TILE, tab, c * 32);
+        else unit_flat(mode_tag, cur, cc * 32, tab, c * 32);
+      }
+    }
+  };
+  for (int t = 0; t < tmask; ++t) tile_body(std::integral_constant<int, kDqInterior>{}, t);
+  for (int t = tmask; t < ntiles; ++t) tile_body(std::integral_constant<int, kDqMasked>{}, t);
+
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt) dq_mfma(dt, dkc[dt], dsh, dsl);
+
+  const int query = q0 + (l & 31);
+  if (query < n) {
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt)
+      store_row(a.out0, hoff + (int64_t)query * sl, a.out_f32, acc[dt], 32 * dt, a.scale);
   }
 }
 
-template <int D, int QB, bool C, bool G, bool SP>
+template <int D, int CPT, bool C, bool G, bool SP>
 static hipError_t launch_one(const KArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((dq_kernel<D, QB, C, G, SP>), dim3(a.nitems), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((dq_kernel<D, CPT, C, G, SP>), dim3(a.nitems), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, int QB>
+template <int D, int CPT>
 static hipError_t dispatch(const KArgs& a, bool c, bool g, bool sp, hipStream_t st) {
   if (c) {
-    if (g) return sp ? launch_one<D, QB, true, true, true>(a, st) : launch_one<D, QB, true, true, false>(a, st);
-    return sp ? launch_one<D, QB, true, false, true>(a, st) : launch_one<D, QB, true, false, false>(a, st);
+    if (g) return sp ? launch_one<D, CPT, true, true, true>(a, st) : launch_one<D, CPT, true, true, false>(a, st);
+    return sp ? launch_one<D, CPT, true, false, true>(a, st) : launch_one<D, CPT, true, false, false>(a, st);
   }
-  if (g) return sp ? launch_one<D, QB, false, true, true>(a, st) : launch_one<D, QB, false, true, false>(a, st);
-  return sp ? launch_one<D, QB, false, false, true>(a, st) : launch_one<D, QB, false, false, false>(a, st);
+  if (g) return sp ? launch_one<D, CPT, false, true, true>(a, st) : launch_one<D, CPT, false, true, false>(a, st);
+  return sp ? launch_one<D, CPT, false, false, true>(a, st) : launch_one<D, CPT, false, false, false>(a, st);
 }
 
-int dq_tile_rows(int d) { return d == 64 ? DqTraits<64, 1>::BM : DqTraits<128, 1>::BM; }
+int dq_tile_rows(int d) { return d == 64 ? DqTraits<64, 2, false>::BM : DqTraits<128, 1, false>::BM; }
 
 hipError_t launch_dq_bf16(const KArgs& a, int d, bool causal, bool gated, bool split,
                           hipStream_t st) {
-  return d == 64 ? dispatch<64, 1>(a, causal, gated, split, st)
+  return d == 64 ? dispatch<64, 2>(a, causal, gated, split, st)
                  : dispatch<128, 1>(a, causal, gated, split, st);
 }
 

@@ -184,39 +184,41 @@ struct DirectTile {
   static constexpr int PER_WAVE = BLOCKS / NWAVES;
   static_assert(BLOCKS % NWAVES == 0, "tile must split evenly over the waves");
 
-  // Per-lane constants: the tile row and the byte offset of the source chunk within it.
-  int row[PER_WAVE];
-  uint32_t col_bytes[PER_WAVE];
-  uint32_t lds_off[PER_WAVE];   // wave-uniform
-
-  __device__ __forceinline__ DirectTile() {
+  // Rows row_base .. row_base + ROWS - 1 of src (element row stride sl, which must keep
+  // ROWS * sl * 2 below 2^32), rows past last_row clamped to last_row. The per-lane
+  // source offsets are recomputed at each call (a few VALU operations per tile) rather
+  // than held in registers.
+  __device__ __forceinline__ static void load(char* lds_tile, const bf16* src, int64_t sl,
+                                              int row_base, int last_row) {
     const int l = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int blk = i * NWAVES + w;
-      const int P = blk * 64 + l;
-      row[i] = P / CPR;
-      col_bytes[i] = (uint32_t)(((P % CPR) ^ xsw<D>(row[i])) * 16);
-      lds_off[i] = (uint32_t)blk * 1024u;
-    }
-  }
-
-  // Rows row_base .. row_base + ROWS - 1 of src (element row stride sl, which must keep
-  // ROWS * sl * 2 below 2^32), rows past last_row clamped to last_row.
-  __device__ __forceinline__ void load(char* lds_tile, const bf16* src, int64_t sl,
-                                       int row_base, int last_row) const {
     const char* base = reinterpret_cast<const char*>(src + (int64_t)row_base * sl);
     const int lim = last_row - row_base;
     const uint32_t rb = (uint32_t)sl * 2u;
     const uint32_t lds = (uint32_t)(uintptr_t)(SA_LDS char*)lds_tile;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int r = row[i] < lim ? row[i] : lim;
-      lds_dma16(base, (uint32_t)r * rb + col_bytes[i], lds + lds_off[i]);
+      const int blk = i * NWAVES + w;
+      const int P = blk * 64 + l;
+      const int row = P / CPR;
+      const uint32_t col = (uint32_t)(((P % CPR) ^ xsw<D>(row)) * 16);
+      const int r = row < lim ? row : lim;
+      lds_dma16(base, (uint32_t)r * rb + col, lds + (uint32_t)blk * 1024u);
     }
   }
 };
+
+// The work item of this workgroup, with every field made explicitly wave-uniform (scalar
+// registers), so that the tensor base pointers derived from it stay in scalar registers.
+__device__ __forceinline__ Item block_item(const KArgs& a) {
+  Item it = decode_item(a, remap_block(blockIdx.x, a.nitems, a.xcd_chunk));
+  it.b = __builtin_amdgcn_readfirstlane(it.b);
+  it.h = __builtin_amdgcn_readfirstlane(it.h);
+  it.t = __builtin_amdgcn_readfirstlane(it.t);
+  it.n = __builtin_amdgcn_readfirstlane(it.n);
+  it.c2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, it.c2)));
+  return it;
+}
 
 // Wait until every vector-memory operation of this wave has completed (including direct
 // loads into LDS), then synchronise the workgroup.

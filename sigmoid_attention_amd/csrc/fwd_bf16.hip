@@ -66,7 +66,7 @@ void fwd_kernel(const KArgs a) {
   const int l = lane_id(), w = wave_id();
   const int lk = 4 * (l >> 5);
   const SplitSel sel;
-  const Item it = decode_item(a, remap_block(blockIdx.x, a.nitems, a.xcd_chunk));
+  const Item it = block_item(a);
   const int n = it.n;
   const int last = n - 1;
   const int64_t hoff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
@@ -91,11 +91,10 @@ void fwd_kernel(const KArgs a) {
     wch = lastq / 32 + 1 < nch ? lastq / 32 + 1 : nch;
   }
 
-  const Tile tile_loader;
   auto issue_tile = [&](int t) {
     char* st = smem + (t % T::NSTAGE) * T::STAGE;
-    tile_loader.load(st, Kg, sl, t * T::BN, last);
-    tile_loader.load(st + T::TILE, Vg, sl, t * T::BN, last);
+    Tile::load(st, Kg, sl, t * T::BN, last);
+    Tile::load(st + T::TILE, Vg, sl, t * T::BN, last);
   };
   // gate table of tile t: logit offset in the exp2 domain (+inf drops the key, which
   // gives P = 0 exactly) and value factor, one entry per key, written by wave 0
