@@ -46,6 +46,12 @@ def parse():
     ap.add_argument("--bf16-out", action="store_true", help="bf16 outputs instead of float")
     ap.add_argument("--also-fast", action="store_true",
                     help="also time fast math with bf16 outputs and report it beside the default")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run a plain copy kernel of known size and 3 launches of each pass, for "
+                         "a rocprofv3 --pmc run (prints nothing else)")
+    ap.add_argument("--pmc-collect", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter_collection.csv files of a FETCH_SIZE run and a "
+                         "WRITE_SIZE run of --pmc-pass into profiles/traffic_<workload>.json")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="lower bound on the oracle time of the CPU baseline sample")
     return ap.parse_args()
@@ -97,6 +103,104 @@ def cpu_baseline(data, w, min_seconds):
     }
 
 
+PASS_KERNELS = {"fwd": "fwd_kernel", "bwd_dq": "dq_kernel", "bwd_dkdv": "dkdv_kernel"}
+COPY_ELEMS = 64 << 20          # float32 elements read and written by the calibration copy
+
+
+def source_hash():
+    """sha256 of the library's kernel and host sources: traffic figures are tied to it."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sigmoid_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def pmc_collect(workload, fetch_csv, write_csv):
+    """HBM bytes per launch of each pass from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by the factor that maps the same counter onto the known bytes of a plain
+    copy (COPY_ELEMS float32 read and written)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                vals.setdefault(name, []).append(float(row["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = COPY_ELEMS * 4
+
+    def pick(vals, key):
+        rows = [v for k, vs in vals.items() if key in k for v in vs]
+        if not rows:
+            raise SystemExit(f"no dispatch of {key} in the counter file")
+        return sum(rows) / len(rows)
+
+    copy_key = "MulFunctor"    # torch's kernel for the calibration multiply
+    f_copy, w_copy = pick(fetch, copy_key), pick(write, copy_key)
+    out = {
+        "workload": workload,
+        "source_hash": source_hash(),
+        "calibration": {"kernel": "torch elementwise multiply (float32, out of place)",
+                        "bytes_read": copy_bytes, "bytes_written": copy_bytes,
+                        "fetch_kib": f_copy, "write_kib": w_copy,
+                        "fetch_factor": copy_bytes / (f_copy * 1024.0),
+                        "write_factor": copy_bytes / (w_copy * 1024.0)},
+        "kernels": {},
+        "command": "rocprofv3 --pmc FETCH_SIZE -d <dir> -o p -f csv -- python3 bench.py --pmc-pass "
+                   f"--workload {workload}; the same with WRITE_SIZE; then python bench.py "
+                   f"--workload {workload} --pmc-collect <fetch csv> <write csv>",
+    }
+    for name, key in PASS_KERNELS.items():
+        fk, wk = pick(fetch, key), pick(write, key)
+        hbm = fk * 1024.0 * out["calibration"]["fetch_factor"] + wk * 1024.0 * out["calibration"]["write_factor"]
+        out["kernels"][name] = {"fetch_kib": fk, "write_kib": wk, "hbm_bytes": hbm}
+    os.makedirs(os.path.dirname(traffic_path(workload)), exist_ok=True)
+    with open(traffic_path(workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def traffic_for(workload, kernel):
+    """Calibrated HBM bytes per launch of `kernel`, or None when no counters were taken for
+    the current sources."""
+    try:
+        with open(traffic_path(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t["kernels"].get(kernel, {}).get("hbm_bytes")
+
+
+def pmc_pass(S, w, t, gate, sl, out_dtype, fast_math):
+    import torch
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=t["q"].device)
+    dst = torch.empty_like(src)
+    torch.mul(src, 2.0, out=dst)
+    kw = dict(causal=w.causal, gate=gate, tau=w.tau, sink=w.sink, out_dtype=out_dtype,
+              fast_math=fast_math)
+    for _ in range(3):
+        S.fwd(t["q"], t["k"], t["v"], sl, **kw)
+        S.bwd_dq(t["q"], t["k"], t["v"], t["do"], sl, **kw)
+        S.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], sl, **kw)
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -104,6 +208,10 @@ def main():
               "collectives and every (batch, head) is independent; run one process per GPU "
               "with its own share of the batch.", file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_collect:
+        pmc_collect(args.workload, *args.pmc_collect)
+        return
 
     import torch
 
@@ -124,6 +232,9 @@ def main():
     out_dtype = torch.bfloat16 if args.bf16_out else torch.float32
     mode = {"inputs": "bf16", "outputs": "bf16" if args.bf16_out else "float32",
             "operands": "bf16" if args.fast_math else "bf16 hi+lo split"}
+    if args.pmc_pass:
+        pmc_pass(S, w, t, gate, sl, out_dtype, args.fast_math)
+        return
     res = measure(S, W, w, t, gate, sl, stream, args.steps, args.warmup, out_dtype,
                   args.fast_math)
     res["mode"] = mode
@@ -218,7 +329,8 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):
         "roofline": {"bound": "mfma", "kernel": dom,
                      "achieved": kernels[dom]["achieved_tflops"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": kernels[dom]["frac_of_peak"], "traffic": None},
+                     "frac": kernels[dom]["frac_of_peak"],
+                     "traffic": traffic_for(w.name, dom)},
         "kernels": kernels,
     }
     return res
