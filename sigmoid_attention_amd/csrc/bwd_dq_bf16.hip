@@ -162,17 +162,18 @@ void dq_kernel(const KArgs a) {
   //   2: entries 4-7, to bf16 (h=0)  | S^T of chunk c+1
   //   3: entries 8-11                | dP^T of chunk c+1
   //   4: entries 12-15, to bf16 (h=1)| dQ for the first key half of chunk c
+  const LdsLane<D> lane;
   auto unit = [&](auto mode_tag, const char* Kc, int krow, const char* Kn, int kn_row,
                   const char* Vn, const float* tab, int kb) {
     bf16x8 kop[T::KS], vop[T::KS], kc0[T::DT], kc1[T::DT];
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lds_row_operand<D>(Kn, kn_row, 16 * ks);
+    for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lane.rowop(Kn, kn_row, ks);
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) kc0[dt] = lds_col_operand<D>(Kc, krow, 32 * dt);
+    for (int dt = 0; dt < T::DT; ++dt) kc0[dt] = lane.colop(Kc, krow, dt);
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) vop[ks] = lds_row_operand<D>(Vn, kn_row, 16 * ks);
+    for (int ks = 0; ks < T::KS; ++ks) vop[ks] = lane.rowop(Vn, kn_row, ks);
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) kc1[dt] = lds_col_operand<D>(Kc, krow + 16, 32 * dt);
+    for (int dt = 0; dt < T::DT; ++dt) kc1[dt] = lane.colop(Kc, krow + 16, dt);
     __builtin_amdgcn_sched_barrier(0);
 
     f32x16 ds;
@@ -215,8 +216,8 @@ void dq_kernel(const KArgs a) {
     dp_cur = zero16();
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
-      s_cur = mfma(lds_row_operand<D>(Kc, krow, 16 * ks), qop[ks], s_cur);
-      dp_cur = mfma(lds_row_operand<D>(Kc + T::TILE, krow, 16 * ks), doop[ks], dp_cur);
+      s_cur = mfma(lane.rowop(Kc, krow, ks), qop[ks], s_cur);
+      dp_cur = mfma(lane.rowop(Kc + T::TILE, krow, ks), doop[ks], dp_cur);
     }
     f32x16 ds;
 #pragma unroll
@@ -227,7 +228,7 @@ void dq_kernel(const KArgs a) {
       to_bf16(ds, h, hi, lo);
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
-        dq_mfma(dt, lds_col_operand<D>(Kc, krow + 16 * h, 32 * dt), hi, lo);
+        dq_mfma(dt, lane.colop(Kc, krow + 16 * h, dt), hi, lo);
     }
   };
   constexpr bool PIPE = D == 64;
@@ -238,13 +239,18 @@ void dq_kernel(const KArgs a) {
   tmask = tmask < ntiles ? tmask : ntiles;
   if (q0 >= n) tmask = 0;
 
-  auto tile_body = [&](auto mode_tag, int t) {
+  // `stage`: the ring slot of tile t, a compile-time constant in the unrolled interior
+  // loop (LDS addresses fold into immediate offsets), or -1 when computed
+  auto tile_body = [&](auto mode_tag, auto stage_tag, int t) {
     constexpr int MODE = decltype(mode_tag)::value;
+    constexpr int SG = decltype(stage_tag)::value;
     if (t > 0) wait_vmem_and_barrier();
     if (t + 2 < ntiles) issue_tile(t + 2);
     if (t + 1 < ntiles) fill_table(t + 1);
-    const char* cur = smem + (t % T::NSTAGE) * T::STAGE;
-    const char* nxt = smem + ((t + 1) % T::NSTAGE) * T::STAGE;
+    const int st = SG >= 0 ? SG : t % T::NSTAGE;
+    const int st1 = SG >= 0 ? (SG + 1) % T::NSTAGE : (t + 1) % T::NSTAGE;
+    const char* cur = smem + st * T::STAGE;
+    const char* nxt = smem + st1 * T::STAGE;
     const float* tab = reinterpret_cast<const float*>(cur + 2 * T::TILE);
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
@@ -257,8 +263,17 @@ void dq_kernel(const KArgs a) {
       }
     }
   };
-  for (int t = 0; t < tmask; ++t) tile_body(std::integral_constant<int, kDqInterior>{}, t);
-  for (int t = tmask; t < ntiles; ++t) tile_body(std::integral_constant<int, kDqMasked>{}, t);
+  using Int = std::integral_constant<int, kDqInterior>;
+  using Msk = std::integral_constant<int, kDqMasked>;
+  using Dyn = std::integral_constant<int, -1>;
+  int t = 0;
+  for (; t + 3 <= tmask; t += 3) {
+    tile_body(Int{}, std::integral_constant<int, 0>{}, t);
+    tile_body(Int{}, std::integral_constant<int, 1>{}, t + 1);
+    tile_body(Int{}, std::integral_constant<int, 2>{}, t + 2);
+  }
+  for (; t < tmask; ++t) tile_body(Int{}, Dyn{}, t);
+  for (; t < ntiles; ++t) tile_body(Msk{}, Dyn{}, t);
 
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) dq_mfma(dt, dkc[dt], dsh, dsl);

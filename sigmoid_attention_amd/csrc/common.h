@@ -112,6 +112,38 @@ __device__ __forceinline__ bf16x8 lds_row_operand(const char* tile, int row0, in
   return lds_read16(tile, swz<D>(row0 + (l & 31), col0 + 8 * (l >> 5)));
 }
 
+// Per-lane byte offsets of the two operand reads above inside a swizzled tile, for row
+// blocks that start at a multiple of 16 rows (the swizzle depends on the low four row
+// bits only, so such a block is the first one shifted by row0 * 2D bytes). With a tile
+// address known at compile time, every read is then one LDS instruction with an
+// immediate offset: no per-read address arithmetic.
+template <int D>
+struct LdsLane {
+  uint32_t row[D / 16];     // row operand of k-step ks
+  uint32_t col[D / 32][2];  // column operand of column block dt: rows r and r + 8
+  __device__ __forceinline__ LdsLane() {
+    const int l = lane_id();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) row[ks] = swz<D>(l & 31, 16 * ks + 8 * (l >> 5));
+    const int g = l >> 4, j = l & 15;
+    const int r = 4 * (g >> 1) + (j >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int c = 32 * dt + 16 * (g & 1) + 4 * (j & 3);
+      col[dt][0] = swz<D>(r, c);
+      col[dt][1] = swz<D>(r + 8, c);
+    }
+  }
+  // row0 must be a multiple of 16
+  __device__ __forceinline__ bf16x8 rowop(const char* tile, int row0, int ks) const {
+    return lds_read16(tile + row0 * (2 * D), row[ks]);
+  }
+  __device__ __forceinline__ bf16x8 colop(const char* tile, int row0, int dt) const {
+    const char* t = tile + row0 * (2 * D);
+    return cat(lds_read_tr(t, col[dt][0]), lds_read_tr(t, col[dt][1]));
+  }
+};
+
 // ---------------------------------------------------------------------------------
 // Staging of a [ROWS][D] bf16 tile: 16-byte global loads into registers (issued one
 // tile ahead, so their latency hides behind the current tile's MFMA work), then

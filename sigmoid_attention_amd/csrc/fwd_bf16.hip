@@ -197,16 +197,17 @@ void fwd_kernel(const KArgs a) {
     if (SPLIT) acc[qb][dt] = mfma(vo, lo, acc[qb][dt]);
   };
 
+  const LdsLane<D> lane;
   auto unit = [&](auto mode_tag, int qb, const char* Kn, int kn_row, int qb_next,
                   const char* Vt, int v_row, const float* tab, int kb) {
     bf16x8 kop[T::KS];
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lds_row_operand<D>(Kn, kn_row, 16 * ks);
+    for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lane.rowop(Kn, kn_row, ks);
     bf16x8 vop0[T::DT], vop1[T::DT];
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) vop0[dt] = lds_col_operand<D>(Vt, v_row, 32 * dt);
+    for (int dt = 0; dt < T::DT; ++dt) vop0[dt] = lane.colop(Vt, v_row, dt);
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) vop1[dt] = lds_col_operand<D>(Vt, v_row + 16, 32 * dt);
+    for (int dt = 0; dt < T::DT; ++dt) vop1[dt] = lane.colop(Vt, v_row + 16, dt);
     __builtin_amdgcn_sched_barrier(0);
 
     f32x16 p;
@@ -262,13 +263,19 @@ void fwd_kernel(const KArgs a) {
   tmask = tmask < ntiles ? tmask : ntiles;
   if (q0 >= n) tmask = 0;                               // nothing to compute
 
-  auto tile_body = [&](auto mode_tag, int t) {
+  // One tile. `stage` is the ring slot of tile t: a compile-time constant in the unrolled
+  // interior loop (the LDS addresses then fold into immediate offsets), or -1 when it
+  // has to be computed.
+  auto tile_body = [&](auto mode_tag, auto stage_tag, int t) {
     constexpr int MODE = decltype(mode_tag)::value;
+    constexpr int SG = decltype(stage_tag)::value;
     if (t > 0) wait_vmem_and_barrier();
     if (t + 2 < ntiles) issue_tile(t + 2);
     if (t + 1 < ntiles) fill_table(t + 1);
-    const char* cur = smem + (t % T::NSTAGE) * T::STAGE;
-    const char* nxt = smem + ((t + 1) % T::NSTAGE) * T::STAGE;
+    const int st = SG >= 0 ? SG : t % T::NSTAGE;
+    const int st1 = SG >= 0 ? (SG + 1) % T::NSTAGE : (t + 1) % T::NSTAGE;
+    const char* cur = smem + st * T::STAGE;
+    const char* nxt = smem + st1 * T::STAGE;
     const float* tab = reinterpret_cast<const float*>(cur + 2 * T::TILE);
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
@@ -280,8 +287,17 @@ void fwd_kernel(const KArgs a) {
       }
     }
   };
-  for (int t = 0; t < tmask; ++t) tile_body(std::integral_constant<int, kInterior>{}, t);
-  for (int t = tmask; t < ntiles; ++t) tile_body(std::integral_constant<int, kMasked>{}, t);
+  using Int = std::integral_constant<int, kInterior>;
+  using Msk = std::integral_constant<int, kMasked>;
+  using Dyn = std::integral_constant<int, -1>;
+  int t = 0;
+  for (; t + 3 <= tmask; t += 3) {
+    tile_body(Int{}, std::integral_constant<int, 0>{}, t);
+    tile_body(Int{}, std::integral_constant<int, 1>{}, t + 1);
+    tile_body(Int{}, std::integral_constant<int, 2>{}, t + 2);
+  }
+  for (; t < tmask; ++t) tile_body(Int{}, Dyn{}, t);
+  for (; t < ntiles; ++t) tile_body(Msk{}, Dyn{}, t);
 
   // the deferred half of the last unit
 #pragma unroll
