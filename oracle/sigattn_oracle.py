@@ -36,6 +36,14 @@ Readings taken where the pages are silent (each is also listed in the design not
 * The backward follows from the forward by the chain rule with the diagonal Jacobian:
   dV'_j = sum_i P_ij dO_i (so dV_j = g_j sum_i P_ij dO_i), dP_ij = dO_i . V'_j,
   dS_ij = dP_ij P_ij (1 - P_ij), dQ_i = s sum_j dS_ij k_j, dK_j = s sum_i dS_ij q_i.
+* The gate gradient (not written out in the pages; the gate is trained, so it is
+  needed) follows by the same chain rule through both places g_j enters:
+  dg_j = sum_i dS_ij / (g_j + eps) + v_j . sum_i P_ij dO_i, per head; the gate is shared
+  by the heads, so the gradient of the shared gate is the sum over heads. The hard drop
+  is a step function of g: a dropped key gets derivative 0, like a padded key.
+* Row mass ([KV-evict] row-sum diagnostic): sum_j P_ij over the allowed keys of query
+  i, i.e. the sum of the attention weights of the row, with the gate's log term in the
+  logits but without the value factor g_j. Padded rows give 0.
 
 All arithmetic is float64 on whatever values are passed in (the GPU's bf16 inputs are
 passed here widened, so both sides see the same bits). Library primitives used as steps:
@@ -64,6 +72,9 @@ __all__ = [
     "forward_rows",
     "dq_rows",
     "dkdv_rows",
+    "gate_grad",
+    "gate_grad_rows",
+    "row_mass",
     "forward_naive",
     "backward_naive",
 ]
@@ -306,6 +317,96 @@ def dkdv_rows(q, k, v, do, seqlens, b, h, key_rows, causal=False, gate=None, tau
     dvp = P.T @ doh
     dv_out[live] = dvp if g is None else dvp * g[cols][:, None]
     return dk_out, dv_out
+
+
+# ----------------------------------------------------------------------------------
+# gate gradient and row mass
+# ----------------------------------------------------------------------------------
+
+def gate_grad(q, k, v, do, seqlens, gate, causal=False, tau=0.0, sink=DEFAULT_SINK,
+              eps=GATE_EPS, scale=None, bias=None, chunk=512):
+    """Derivative of sum(dO * O) with respect to the per-key gate g[b, j].
+
+    g_j enters twice ([KV-evict] gate paragraphs): x_ij += log(g_j + eps) and
+    V'_j = g_j v_j. By the chain rule, per head h,
+        dg_hj = sum_i dS_ij / (g_j + eps)  +  v_j . sum_i P_ij dO_i
+    with dS_ij = (dO_i . V'_j) P_ij (1 - P_ij) as in the backward. The gate is shared by
+    the heads, so dg_j = sum_h dg_hj.
+
+    Returns (dg_head [B, H, L], dg [B, L]); padded and dropped keys give exactly 0.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    if gate is None:
+        raise ValueError("gate_grad needs a gate")
+    B, H, L, d = q.shape
+    s = _params(d, scale)
+    dg_head = np.zeros((B, H, L))
+    for b in range(B):
+        n = int(seqlens[b])
+        if n == 0:
+            continue
+        beta, g, keep, logg = _head_setup(b, n, L, gate, tau, sink, bias, eps)
+        cols = np.arange(n)
+        for h in range(H):
+            kh, vh = k[b, h, :n], v[b, h, :n]
+            vp = _vprime(vh, g, cols)
+            sum_ds = np.zeros(n)          # sum_i dS_ij
+            pdo = np.zeros((n, d))        # sum_i P_ij dO_i
+            for r0 in range(0, n, chunk):
+                rows = np.arange(r0, min(n, r0 + chunk))
+                P = _P(q[b, h, rows], kh, rows, cols, s, beta, logg, keep, causal)
+                dS = (do[b, h, rows] @ vp.T) * P * (1.0 - P)
+                sum_ds += dS.sum(axis=0)
+                pdo += P.T @ do[b, h, rows]
+            grad = sum_ds / (g[:n] + eps) + np.einsum("jc,jc->j", vh, pdo)
+            dg_head[b, h, :n] = np.where(keep[:n], grad, 0.0)
+    return dg_head, dg_head.sum(axis=1)
+
+
+def gate_grad_rows(q, k, v, do, seqlens, gate, b, h, key_rows, causal=False, tau=0.0,
+                   sink=DEFAULT_SINK, eps=GATE_EPS, scale=None, bias=None):
+    """dg_head[b, h, key_rows] (see gate_grad) from all valid queries of (b, h)."""
+    key_rows = np.asarray(key_rows, dtype=np.int64)
+    out = np.zeros(len(key_rows))
+    n = int(seqlens[b])
+    if n == 0:
+        return out
+    d = q.shape[-1]
+    s = _params(d, scale)
+    beta, g, keep, logg = _head_setup(b, n, q.shape[2], gate, tau, sink, bias, eps)
+    live = key_rows < n
+    cols = key_rows[live]
+    rows = np.arange(n)
+    qh, doh = _as64(q[b, h, :n]), _as64(do[b, h, :n])
+    kc, vc = _as64(k[b, h, cols]), _as64(v[b, h, cols])
+    P = _P(qh, kc, rows, cols, s, beta, logg, keep, causal)
+    dS = (doh @ (vc * g[cols][:, None]).T) * P * (1.0 - P)
+    grad = dS.sum(axis=0) / (g[cols] + eps) + np.einsum("jc,jc->j", vc, P.T @ doh)
+    out[live] = np.where(keep[cols], grad, 0.0)
+    return out
+
+
+def row_mass(q, k, seqlens, causal=False, gate=None, tau=0.0, sink=DEFAULT_SINK,
+             eps=GATE_EPS, scale=None, bias=None, chunk=512):
+    """R[b, h, i] = sum_j P_ij over the allowed keys of query i ([KV-evict] row-sum
+    diagnostic: under the sigmoid the row mass is free to vary with the query).
+    Returns float64 [B, H, L]; rows i >= n_b are exactly 0."""
+    q, k = _as64(q), _as64(k)
+    B, H, L, d = q.shape
+    s = _params(d, scale)
+    R = np.zeros((B, H, L))
+    for b in range(B):
+        n = int(seqlens[b])
+        if n == 0:
+            continue
+        beta, g, keep, logg = _head_setup(b, n, L, gate, tau, sink, bias, eps)
+        cols = np.arange(n)
+        for h in range(H):
+            for r0 in range(0, n, chunk):
+                rows = np.arange(r0, min(n, r0 + chunk))
+                P = _P(q[b, h, rows], k[b, h, :n], rows, cols, s, beta, logg, keep, causal)
+                R[b, h, rows] = P.sum(axis=1)
+    return R
 
 
 # ----------------------------------------------------------------------------------

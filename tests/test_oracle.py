@@ -452,3 +452,147 @@ def test_absolute_sums():
                 dk, dv = O.dkdv_rows(q, k, v, do, seqlens, b, h, rows, absolute=True, **kw)
                 np.testing.assert_allclose(dk, mags[1][b, h], rtol=1e-11, atol=1e-15)
                 np.testing.assert_allclose(dv, mags[2][b, h], rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------------
+# gate gradient and row mass
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["bidir", "causal", "drop"])
+def test_gate_grad_finite_differences(variant):
+    """Central differences of L = <dO, O> with respect to the shared gate g[b, j] match
+    dg = sum_h dg_h (gate injection of the KV-eviction paper: log g on the logits, g on
+    the values). Several heads, so the head sum is exercised; in the drop variant some
+    gates sit far below tau, where the loss does not depend on them (derivative 0)."""
+    B, H, L, d = 2, 3, 8, 4
+    seqlens = [8, 6]
+    q, k, v, do = (_rand((B, H, L, d), 50 + s) for s in range(4))
+    g = np.random.default_rng(60).uniform(0.2, 1.0, (B, L))
+    kw = dict(gate=g)
+    if variant == "causal":
+        kw["causal"] = True
+    if variant == "drop":
+        g[0, 5] = g[1, 2] = 0.01
+        kw.update(tau=0.05, sink=1, causal=True)
+    dg_head, dg = O.gate_grad(q, k, v, do, seqlens, **kw)
+    np.testing.assert_allclose(dg, dg_head.sum(axis=1), rtol=1e-14, atol=0)
+
+    def loss(gg):
+        kk = dict(kw, gate=gg)
+        return float(np.sum(do * O.forward(q, k, v, seqlens, **kk)))
+
+    h = 1e-6
+    num = np.zeros_like(g)
+    for idx in np.ndindex(g.shape):
+        gp, gm = g.copy(), g.copy()
+        gp[idx] += h
+        gm[idx] -= h
+        num[idx] = (loss(gp) - loss(gm)) / (2 * h)
+    np.testing.assert_allclose(dg, num, rtol=1e-6, atol=1e-8)
+    if variant == "drop":
+        assert dg[0, 5] == 0.0 and dg[1, 2] == 0.0
+        assert np.all(dg_head[:, :, 5][0] == 0.0)
+    for b, n in enumerate(seqlens):
+        assert np.all(dg_head[b, :, n:] == 0.0)
+
+
+def test_gate_grad_scaling_identity():
+    """With eps = 0, scaling every gate by lam equals adding ln(lam) to the bias and
+    scaling O by lam, so L(lam g) = lam L_{beta + ln lam}(g). Differentiating at lam = 1:
+    sum_j g_j dg_j = L + dL/dbeta, where dL/dbeta is taken by central differences of the
+    forward in the bias (an independent route to the same number)."""
+    B, H, L, d = 2, 2, 10, 4
+    seqlens = [10, 7]
+    q, k, v, do = (_rand((B, H, L, d), 70 + s) for s in range(4))
+    g = np.random.default_rng(80).uniform(0.1, 1.0, (B, L))
+    kw = dict(gate=g, eps=0.0)
+    for causal in (False, True):
+        _, dg = O.gate_grad(q, k, v, do, seqlens, causal=causal, **kw)
+        for b, n in enumerate(seqlens):
+            beta = np.array([O.sequence_bias(m) for m in seqlens])
+
+            def loss(bb):
+                o = O.forward(q, k, v, seqlens, causal=causal, bias=bb, **kw)
+                return float(np.sum(do[b] * o[b]))
+
+            h = 1e-6
+            bp, bm = beta.copy(), beta.copy()
+            bp[b] += h
+            bm[b] -= h
+            dbeta = (loss(bp) - loss(bm)) / (2 * h)
+            lhs = float(np.sum(g[b, :n] * dg[b, :n]))
+            assert lhs == pytest.approx(loss(beta) + dbeta, rel=1e-7, abs=1e-9)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gate_grad_closed_form_qk_zero(causal):
+    """Q = K = 0: every P_ij = p_j = (g_j+eps)/(n+g_j+eps), so for each head
+    dg_j = (sum over allowed i of dO_i) . v_j * (p_j + g_j p_j (1-p_j)/(g_j+eps))."""
+    rng = np.random.default_rng(14)
+    B, H, L, d, n = 1, 2, 9, 4, 8
+    g = rng.uniform(0.05, 1.0, (B, L))
+    z = np.zeros((B, H, L, d))
+    v, do = rng.standard_normal((B, H, L, d)), rng.standard_normal((B, H, L, d))
+    eps = O.GATE_EPS
+    dg_head, _ = O.gate_grad(z, z, v, do, [n], gate=g, causal=causal)
+    p = (g[0] + eps) / (n + g[0] + eps)
+    for h in range(H):
+        for j in range(L):
+            if j >= n:
+                assert dg_head[0, h, j] == 0.0
+                continue
+            lo = j if causal else 0
+            sdo = do[0, h, lo:n].sum(axis=0)
+            want = float(sdo @ v[0, h, j]) * (p[j] + g[0, j] * p[j] * (1 - p[j]) / (g[0, j] + eps))
+            assert dg_head[0, h, j] == pytest.approx(want, rel=1e-12, abs=1e-14)
+
+
+def test_gate_grad_rows_match_full():
+    B, H, L, d = 2, 2, 33, 8
+    seqlens = [33, 20]
+    q, k, v, do = (_rand((B, H, L, d), 90 + s) for s in range(4))
+    g = np.random.default_rng(95).uniform(0.0, 1.0, (B, L))
+    for kw in (dict(), dict(causal=True, tau=0.3, sink=4)):
+        dg_head, _ = O.gate_grad(q, k, v, do, seqlens, gate=g, chunk=7, **kw)
+        rows = np.array([0, 3, 19, 20, 32])
+        for b in range(B):
+            for h in range(H):
+                got = O.gate_grad_rows(q, k, v, do, seqlens, g, b, h, rows, **kw)
+                np.testing.assert_allclose(got, dg_head[b, h, rows], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_mass_closed_form_qk_zero(causal):
+    """Q = K = 0: each allowed weight is sigma(-ln n) = 1/(n+1), so the row mass is
+    n/(n+1) (bidirectional) or (i+1)/(n+1) (causal); with a gate it is
+    sum over allowed kept j of (g_j+eps)/(n+g_j+eps)."""
+    B, H, L, d = 2, 2, 12, 4
+    seqlens = [12, 5]
+    z = np.zeros((B, H, L, d))
+    R = O.row_mass(z, z, seqlens, causal=causal)
+    g = np.random.default_rng(15).uniform(0.0, 1.0, (B, L))
+    Rg = O.row_mass(z, z, seqlens, causal=causal, gate=g, tau=0.3, sink=2)
+    eps = O.GATE_EPS
+    for b, n in enumerate(seqlens):
+        keep = O.kept_keys(n, L, g[b], 0.3, 2)
+        for i in range(L):
+            if i >= n:
+                assert np.all(R[b, :, i] == 0.0) and np.all(Rg[b, :, i] == 0.0)
+                continue
+            hi = i + 1 if causal else n
+            np.testing.assert_allclose(R[b, :, i], hi / (n + 1), rtol=1e-14)
+            js = [j for j in range(hi) if keep[j]]
+            want = sum((g[b, j] + eps) / (n + g[b, j] + eps) for j in js)
+            np.testing.assert_allclose(Rg[b, :, i], want, rtol=1e-13)
+
+
+def test_row_mass_is_forward_with_unit_values():
+    """Ungated, the row mass is the output for V = 1 in every feature."""
+    B, H, L, d = 2, 2, 20, 8
+    seqlens = [20, 9]
+    q, k = _rand((B, H, L, d), 100), _rand((B, H, L, d), 101)
+    for causal in (False, True):
+        R = O.row_mass(q, k, seqlens, causal=causal, chunk=6)
+        o = O.forward(q, k, np.ones((B, H, L, d)), seqlens, causal=causal)
+        for c in range(d):
+            np.testing.assert_allclose(R, o[..., c], rtol=1e-13, atol=0)
