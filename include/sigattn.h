@@ -101,6 +101,18 @@ sigattn_status sigattn_validate(const sigattn_problem* p);
 sigattn_status sigattn_fwd(const sigattn_problem* p, const void* q, const void* k,
                            const void* v, void* o, void* stream);
 
+/* Forward plus the row mass of every query: row_mass[b][h][i] = sum_j P_ij over the
+ * allowed keys of query i (the attention weights, with the gate's log term in the
+ * logits but without the value factor g_j). Without row normalisation this total is
+ * free to vary from query to query ("Sigmoid Attention as a Better Substrate for
+ * Learned KV Cache Eviction", row-sum diagnostic); its spread across queries is what
+ * that diagnostic reports. o is exactly that of sigattn_fwd.
+ *  row_mass  DEVICE float [B][H][Lmax], dense (entry (b,h,i) at (b*H + h)*Lmax + i),
+ *            4-byte aligned, fully written: 0 for i >= n_b. Must not alias another
+ *            argument. */
+sigattn_status sigattn_fwd_rowsum(const sigattn_problem* p, const void* q, const void* k,
+                                  const void* v, void* o, float* row_mass, void* stream);
+
 /* Backward, query side: dq = s sum_j dS_ij k_j, recomputing P (no stored attention).
  * Rows i >= n_b of dq are written as 0. Paper: section 4, backward decomposition. */
 sigattn_status sigattn_bwd_dq(const sigattn_problem* p, const void* q, const void* k,
@@ -112,6 +124,24 @@ sigattn_status sigattn_bwd_dq(const sigattn_problem* p, const void* q, const voi
 sigattn_status sigattn_bwd_dkdv(const sigattn_problem* p, const void* q, const void* k,
                                 const void* v, const void* dout, void* dk, void* dv,
                                 void* stream);
+
+/* Backward, key side, plus the gradient of the per-key gate (requires p->gate).
+ * g_j enters twice, as log(g_j + eps) on the logits and as the factor g_j on v_j; by the
+ * chain rule (diagonal Jacobian as above) the derivative of sum(dO * O) over head h is
+ *   dg_head[b][h][j] = sum_i dS_ij / (g_j + eps) + v_j . sum_i P_ij dO_i
+ * ("Sigmoid Attention as a Better Substrate for Learned KV Cache Eviction", gate
+ * paragraphs: the gates are trained with the model). dk and dv are exactly those of
+ * sigattn_bwd_dkdv.
+ *  dg_head  DEVICE float [B][H][Lmax], dense (entry (b,h,j) at (b*H + h)*Lmax + j),
+ *           4-byte aligned, fully written: 0 for j >= n_b and for dropped keys (the
+ *           drop is a step in g, derivative 0).
+ *  dg       DEVICE float [B][Lmax], dense, or NULL: the gradient of the gate shared by
+ *           the heads, dg[b][j] = sum over h of dg_head[b][h][j], summed in head order
+ *           (deterministic). 4-byte aligned.
+ * Neither may alias another argument. Returns SIGATTN_ERR_INVALID_ARG without a gate. */
+sigattn_status sigattn_bwd_dkdv_dg(const sigattn_problem* p, const void* q, const void* k,
+                                   const void* v, const void* dout, void* dk, void* dv,
+                                   float* dg_head, float* dg, void* stream);
 
 /* Host-side view of the work list a pass launches, for inspection and tests.
  * pass: 0 forward, 1 dq, 2 dk/dv. Writes up to `cap` items as (b, h, tile) int32

@@ -324,7 +324,7 @@ def dkdv_rows(q, k, v, do, seqlens, b, h, key_rows, causal=False, gate=None, tau
 # ----------------------------------------------------------------------------------
 
 def gate_grad(q, k, v, do, seqlens, gate, causal=False, tau=0.0, sink=DEFAULT_SINK,
-              eps=GATE_EPS, scale=None, bias=None, chunk=512):
+              eps=GATE_EPS, scale=None, bias=None, chunk=512, absolute=False):
     """Derivative of sum(dO * O) with respect to the per-key gate g[b, j].
 
     g_j enters twice ([KV-evict] gate paragraphs): x_ij += log(g_j + eps) and
@@ -334,6 +334,9 @@ def gate_grad(q, k, v, do, seqlens, gate, causal=False, tau=0.0, sink=DEFAULT_SI
     the heads, so dg_j = sum_h dg_hj.
 
     Returns (dg_head [B, H, L], dg [B, L]); padded and dropped keys give exactly 0.
+
+    absolute=True returns the magnitude sums sum_i |dS_ij| / (g_j + eps) +
+    sum_i P_ij |dO_i . v_j| instead, which bound how rounding of dS or P propagates.
     """
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
     if gate is None:
@@ -356,9 +359,16 @@ def gate_grad(q, k, v, do, seqlens, gate, causal=False, tau=0.0, sink=DEFAULT_SI
                 rows = np.arange(r0, min(n, r0 + chunk))
                 P = _P(q[b, h, rows], kh, rows, cols, s, beta, logg, keep, causal)
                 dS = (do[b, h, rows] @ vp.T) * P * (1.0 - P)
-                sum_ds += dS.sum(axis=0)
-                pdo += P.T @ do[b, h, rows]
-            grad = sum_ds / (g[:n] + eps) + np.einsum("jc,jc->j", vh, pdo)
+                if absolute:
+                    sum_ds += np.abs(dS).sum(axis=0)
+                    pdo[:, 0] += np.sum(P * np.abs(do[b, h, rows] @ vh.T), axis=0)
+                else:
+                    sum_ds += dS.sum(axis=0)
+                    pdo += P.T @ do[b, h, rows]
+            if absolute:
+                grad = sum_ds / (g[:n] + eps) + pdo[:, 0]
+            else:
+                grad = sum_ds / (g[:n] + eps) + np.einsum("jc,jc->j", vh, pdo)
             dg_head[b, h, :n] = np.where(keep[:n], grad, 0.0)
     return dg_head, dg_head.sum(axis=1)
 

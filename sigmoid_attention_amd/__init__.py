@@ -7,8 +7,10 @@ raises, there is no fallback.
 
     o = fwd(q, k, v, seqlens, causal=False, gate=None, tau=0.0, sink=4,
             out_dtype=None, fast_math=False)
+    o, row_mass = fwd_rowsum(q, k, v, seqlens, ...)
     dq = bwd_dq(q, k, v, do, seqlens, ...)
     dk, dv = bwd_dkdv(q, k, v, do, seqlens, ...)
+    dk, dv, dg_head, dg = bwd_dkdv_dg(q, k, v, do, seqlens, gate=g, ...)
 
 Tensors are [B, H, Lmax, d] views (any strides with a contiguous last dimension, the
 same strides for all of them), bf16 or float32 (the float32 debug path), on one GPU.
@@ -23,7 +25,7 @@ import os
 
 import numpy as np
 
-__all__ = ["fwd", "bwd_dq", "bwd_dkdv", "validate", "plan", "library_path", "load",
+__all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd_dkdv_dg", "validate", "plan", "library_path", "load",
            "Problem", "SigattnError", "STATUS", "VERSION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,15 +85,18 @@ def load():
     vp = ctypes.c_void_p
     lib.sigattn_validate.argtypes = [P]
     lib.sigattn_fwd.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.sigattn_fwd_rowsum.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_bwd_dkdv_dg.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sigattn_plan.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                  ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]
     lib.sigattn_plan.restype = ctypes.c_int64
     lib.sigattn_status_string.argtypes = [ctypes.c_int]
     lib.sigattn_status_string.restype = ctypes.c_char_p
     lib.sigattn_version.restype = ctypes.c_int
-    for f in (lib.sigattn_validate, lib.sigattn_fwd, lib.sigattn_bwd_dq, lib.sigattn_bwd_dkdv):
+    for f in (lib.sigattn_validate, lib.sigattn_fwd, lib.sigattn_fwd_rowsum, lib.sigattn_bwd_dq,
+              lib.sigattn_bwd_dkdv, lib.sigattn_bwd_dkdv_dg):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -264,3 +269,70 @@ def bwd_dkdv(q, k, v, do, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, 
     del keep
     _check(code, "sigattn_bwd_dkdv")
     return dk, dv
+
+
+def _new_plane(q, shape):
+    torch = _torch()
+    return torch.empty(shape, dtype=torch.float32, device=q.device)
+
+
+def _check_plane(q, t, shape):
+    torch = _torch()
+    if (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or t.device != q.device
+            or not t.is_contiguous()):
+        raise ValueError(f"expected a contiguous float32 tensor of shape {tuple(shape)} on q's GPU")
+
+
+def bwd_dkdv_dg(q, k, v, do, seqlens, *, gate, causal=False, tau=0.0, sink=4, eps=1e-8,
+                scale=0.0, bias=None, out=None, dg_head=None, dg=None, out_dtype=None,
+                fast_math=False, head_sum=True):
+    """(dK, dV, dg_head, dg): dK and dV as bwd_dkdv, plus the gate gradient per head
+    ([B, H, Lmax] float32) and summed over heads ([B, Lmax] float32, None when
+    head_sum is False)."""
+    if gate is None:
+        raise ValueError("bwd_dkdv_dg needs a gate")
+    lib = load()
+    prob, keep = _describe(q, (k, v, do), seqlens, causal, gate, tau, sink, eps, scale, bias,
+                           out_dtype, fast_math)
+    dk, dv = (_new_out(q, out_dtype), _new_out(q, out_dtype)) if out is None else out
+    _check_out(q, dk, out_dtype)
+    _check_out(q, dv, out_dtype)
+    B, H, L, _ = q.shape
+    if dg_head is None:
+        dg_head = _new_plane(q, (B, H, L))
+    _check_plane(q, dg_head, (B, H, L))
+    if head_sum:
+        if dg is None:
+            dg = _new_plane(q, (B, L))
+        _check_plane(q, dg, (B, L))
+    else:
+        dg = None
+    code = lib.sigattn_bwd_dkdv_dg(ctypes.byref(prob), q.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), do.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                   dg_head.data_ptr(), None if dg is None else dg.data_ptr(),
+                                   _stream(q))
+    del keep
+    _check(code, "sigattn_bwd_dkdv_dg")
+    return dk, dv, dg_head, dg
+
+
+def fwd_rowsum(q, k, v, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, eps=1e-8,
+               scale=0.0, bias=None, out=None, row_mass=None, out_dtype=None,
+               fast_math=False):
+    """(O, row_mass): O as fwd, plus sum_j P_ij per query ([B, H, Lmax] float32)."""
+    lib = load()
+    prob, keep = _describe(q, (k, v), seqlens, causal, gate, tau, sink, eps, scale, bias,
+                           out_dtype, fast_math)
+    if out is None:
+        out = _new_out(q, out_dtype)
+    _check_out(q, out, out_dtype)
+    B, H, L, _ = q.shape
+    if row_mass is None:
+        row_mass = _new_plane(q, (B, H, L))
+    _check_plane(q, row_mass, (B, H, L))
+    code = lib.sigattn_fwd_rowsum(ctypes.byref(prob), q.data_ptr(), k.data_ptr(),
+                                  v.data_ptr(), out.data_ptr(), row_mass.data_ptr(),
+                                  _stream(q))
+    del keep
+    _check(code, "sigattn_fwd_rowsum")
+    return out, row_mass

@@ -18,6 +18,15 @@ struct ZArgs {
   uint16_t len[kMaxBatch];   // valid length by batch index
 };
 
+// Per-head float planes [B][H][Lmax] (gate gradient, row mass): zero the entries
+// j >= n_b and, when sum is set, write sum[b][j] = sum over h of plane[b][h][j].
+struct PArgs {
+  float* plane;
+  float* sum;            // [B][Lmax] or null
+  int32_t B, H, Lmax;
+  uint16_t len[kMaxBatch];   // valid length by batch index
+};
+
 struct DArgs {
   const void* q;
   const void* k;
@@ -25,6 +34,7 @@ struct DArgs {
   const void* dout;
   void* out0;
   void* out1;
+  float* aux;            // dg plane of the dk/dv pass, row-mass plane of the forward
   const float* gate;
   int64_t sb, sh, sl, gsb;
   int32_t B, H, Lmax, d;

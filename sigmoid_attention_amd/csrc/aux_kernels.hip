@@ -3,6 +3,9 @@
 //    outputs, so that every output element is defined. Padded input slots are never
 //    read (padded tiles are skipped, "Better Models, Faster Training: Sigmoid Attention
 //    for single-cell Foundation Models", section 4).
+//  * plane_tail: per-head float planes [B][H][Lmax] (gate gradient, row mass): zeros
+//    for j >= n_b, and the sum over heads of the gate gradient, in head order (the gate
+//    is shared by the heads, so its gradient is the sum of the per-head ones).
 //  * the float32 debug path: one wave per output row, plain loops with a wave-wide
 //    reduction for each dot product. It is slow and simple on purpose; it computes the
 //    same definitions as the bf16 kernels (section 3 equation; gate injection and
@@ -35,6 +38,26 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(const ZArgs z) {
 hipError_t launch_zero_rows(const ZArgs& z, int B, int H, hipStream_t st) {
   dim3 grid((z.Lmax + kZeroRows - 1) / kZeroRows, H, B);
   hipLaunchKernelGGL(zero_rows_kernel, grid, dim3(256), 0, st, z);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void plane_tail_kernel(const PArgs pa) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= pa.Lmax) return;
+  const int n = pa.len[b];
+  float* row = pa.plane + (int64_t)b * pa.H * pa.Lmax + j;
+  float acc = 0.0f;
+  for (int h = 0; h < pa.H; ++h) {
+    if (j >= n) row[(int64_t)h * pa.Lmax] = 0.0f;
+    else acc += row[(int64_t)h * pa.Lmax];
+  }
+  if (pa.sum) pa.sum[(int64_t)b * pa.Lmax + j] = acc;
+}
+
+hipError_t launch_plane_tail(const PArgs& pa, hipStream_t st) {
+  dim3 grid((pa.Lmax + 255) / 256, pa.B);
+  hipLaunchKernelGGL(plane_tail_kernel, grid, dim3(256), 0, st, pa);
   return hipGetLastError();
 }
 
@@ -92,9 +115,11 @@ __global__ __launch_bounds__(256) void f32_kernel(const DArgs a, int pass) {
   constexpr int MAXC = 2;  // d / 64 elements per lane, d <= 128
   float acc0[MAXC] = {0.0f, 0.0f}, acc1[MAXC] = {0.0f, 0.0f};
 
+  const int64_t plane_idx = ((int64_t)b * a.H + h) * a.Lmax + i;
   if (pass == 0 || pass == 1) {
     const float* qi = Q + (int64_t)i * sl;
     const float* doi = dO + (int64_t)i * sl;
+    float mass = 0.0f;
     for (int j = 0; j < n; ++j) {
       if (a.causal && j > i) break;
       if (!rule.kept(j)) continue;
@@ -102,6 +127,7 @@ __global__ __launch_bounds__(256) void f32_kernel(const DArgs a, int pass) {
       const float* vj = V + (int64_t)j * sl;
       const float p = logistic(rule.logit(row_dot(qi, kj, a.d, lane), j));
       const float g = rule.gate(j);
+      mass += p;
       if (pass == 0) {
         for (int c = lane, e = 0; c < a.d; c += 64, ++e) acc0[e] = fmaf(p * g, vj[c], acc0[e]);
       } else {
@@ -112,18 +138,21 @@ __global__ __launch_bounds__(256) void f32_kernel(const DArgs a, int pass) {
     float* out = (float*)a.out0 + hoff + (int64_t)i * sl;
     const float mul = pass == 0 ? 1.0f : a.scale;
     for (int c = lane, e = 0; c < a.d; c += 64, ++e) out[c] = acc0[e] * mul;
+    if (pass == 0 && a.aux && lane == 0) a.aux[plane_idx] = mass;
   } else {
     const int j = i;  // this wave owns key row j
     const float* kj = K + (int64_t)j * sl;
     const float* vj = V + (int64_t)j * sl;
     const bool keep = rule.kept(j);
     const float g = rule.gate(j);
+    float ds_sum = 0.0f;
     if (keep) {
       for (int qi_ = a.causal ? j : 0; qi_ < n; ++qi_) {
         const float* qi = Q + (int64_t)qi_ * sl;
         const float* doi = dO + (int64_t)qi_ * sl;
         const float p = logistic(rule.logit(row_dot(qi, kj, a.d, lane), j));
         const float ds = g * row_dot(doi, vj, a.d, lane) * p * (1.0f - p);
+        ds_sum += ds;
         for (int c = lane, e = 0; c < a.d; c += 64, ++e) {
           acc1[e] = fmaf(p, doi[c], acc1[e]);   // dV before the gate factor
           acc0[e] = fmaf(ds, qi[c], acc0[e]);   // dK before the scale
@@ -135,6 +164,13 @@ __global__ __launch_bounds__(256) void f32_kernel(const DArgs a, int pass) {
     for (int c = lane, e = 0; c < a.d; c += 64, ++e) {
       dk[c] = keep ? acc0[e] * a.scale : 0.0f;
       dv[c] = keep ? acc1[e] * g : 0.0f;
+    }
+    if (a.aux) {
+      // gate gradient: sum_i dS_ij / (g_j + eps) + v_j . sum_i P_ij dO_i
+      float vd = 0.0f;
+      for (int c = lane, e = 0; c < a.d; c += 64, ++e) vd = fmaf(vj[c], acc1[e], vd);
+      vd = wave_sum(vd);
+      if (lane == 0) a.aux[plane_idx] = keep ? ds_sum / (g + a.gate_eps) + vd : 0.0f;
     }
   }
 }

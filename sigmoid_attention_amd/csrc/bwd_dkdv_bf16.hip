@@ -13,6 +13,13 @@
 // c (a unit): the logistic function of S(c) runs while the MFMAs of dP(c) and S(c+1)
 // execute; then dS, the bf16 operands, and dV^T += dO^T P, dK^T += Q^T dS (dO^T and Q^T
 // read with transposed LDS loads).
+//
+// With DG the pass also writes the per-head gate gradient
+//   dg_hj = sum_i dS_ij / (g_j + eps) + v_j . sum_i P_ij dO_i
+// (chain rule through both places the gate enters: log g_j on the logits and g_j on the
+// values, "Sigmoid Attention as a Better Substrate for Learned KV Cache Eviction", gate
+// paragraphs): each lane sums the float dS of its key column as it goes, and the dot
+// product with v_j reads the dV accumulator before the gate factor in the epilogue.
 #include <type_traits>
 
 #include "common.h"
@@ -38,7 +45,7 @@ __device__ __forceinline__ constexpr int kv_arc(int r) { return 8 * (r >> 2) + (
 
 // K, V, dK and dV of 32 keys take 96 registers per lane at d = 64 (two waves per SIMD)
 // and 192 at d = 128 (one wave per SIMD).
-template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT>
+template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool DG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
 void dkdv_kernel(const KArgs a) {
   using T = DkvTraits<D, CPT>;
@@ -64,13 +71,14 @@ void dkdv_kernel(const KArgs a) {
   const float c1 = a.c1;
 
   // per-lane key constants: logit offset (exp2 domain; +inf drops the key) and factor
-  float c2 = it.c2, gmul = 1.0f;
+  float c2 = it.c2, gmul = 1.0f, gval = 1.0f;
   if (GATED) {
-    const float g = a.gate[(int64_t)it.b * a.gsb + (mykey < last ? mykey : last)];
-    const bool keep = mykey < n && !(mykey >= a.gate_sink && g < a.gate_tau);
-    c2 = keep ? c2 - __builtin_amdgcn_logf(g + a.gate_eps) : __builtin_inff();
-    gmul = keep ? g : 0.0f;
+    gval = a.gate[(int64_t)it.b * a.gsb + (mykey < last ? mykey : last)];
+    const bool keep = mykey < n && !(mykey >= a.gate_sink && gval < a.gate_tau);
+    c2 = keep ? c2 - __builtin_amdgcn_logf(gval + a.gate_eps) : __builtin_inff();
+    gmul = keep ? gval : 0.0f;
   }
+  float ds_sum = 0.0f;   // DG: sum over this lane's queries of dS / g_j
 
   // query chunks of the item: all valid queries, or (causal) those from the item's
   // first key on; this wave's first contributing chunk is c_lo
@@ -139,6 +147,18 @@ void dkdv_kernel(const KArgs a) {
       p[r] = x;
     }
   };
+  // masked entries have P = 0 and a finite dP, so their dS is exactly 0
+  auto accumulate_ds = [&](const f32x16& ds) {
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 4) {
+      s0 += ds[r];
+      s1 += ds[r + 1];
+      s2 += ds[r + 2];
+      s3 += ds[r + 3];
+    }
+    ds_sum += (s0 + s1) + (s2 + s3);
+  };
   auto to_bf16 = [&](const f32x16& v, int h, bf16x8& hi, bf16x8& lo) {
     if (SPLIT) split8(v, 8 * h, hi, lo, sel);
     else hi = pack8(v, 8 * h);
@@ -180,6 +200,7 @@ void dkdv_kernel(const KArgs a) {
     f32x16 ds;
 #pragma unroll
     for (int r = 0; r < 16; ++r) ds[r] = dp[r] * __builtin_fmaf(-p[r], p[r], p[r]);
+    if (DG) accumulate_ds(ds);
     bf16x8 ph0, pl0, dh0, dl0, ph1, pl1, dh1, dl1;
     to_bf16(p, 0, ph0, pl0);
     to_bf16(ds, 0, dh0, dl0);
@@ -222,6 +243,7 @@ void dkdv_kernel(const KArgs a) {
     sig16(mode_tag, qb0, p);
 #pragma unroll
     for (int r = 0; r < 16; ++r) ds[r] = dp[r] * __builtin_fmaf(-p[r], p[r], p[r]);
+    if (DG) accumulate_ds(ds);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 ph, pl, dh, dl;
@@ -268,6 +290,30 @@ void dkdv_kernel(const KArgs a) {
   for (int t = tm1; t < tm2; ++t) tile_body(std::integral_constant<int, kKvInterior>{}, t);
   for (int t = tm2; t < ntiles; ++t) tile_body(std::integral_constant<int, kKvMasked>{}, t);
 
+  if (DG) {
+    // v_j . (sum_i P_ij dO_i): this lane holds features 32 dt + 8 m + lk + e of the dV
+    // accumulator (before the gate factor); the partner lane (l ^ 32) holds the rest
+    float vdot = 0.0f;
+    if (mykey < n) {
+      const bf16* vr = Vg + (int64_t)mykey * sl + lk;
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(vr + 32 * dt + 8 * m);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vdot = __builtin_fmaf((float)v4[e], dv[dt][4 * m + e], vdot);
+        }
+    }
+    ds_sum += __shfl_xor(ds_sum, 32, 64);
+    vdot += __shfl_xor(vdot, 32, 64);
+    if (l < 32 && mykey < n) {
+      // dS = g_j * ds_sum terms (the kernel's dP omits the gate factor of V'_j)
+      const float dg = gmul != 0.0f ? gval / (gval + a.gate_eps) * ds_sum + vdot : 0.0f;
+      a.aux[((int64_t)it.b * a.H + it.h) * a.Lmax + mykey] = dg;
+    }
+  }
+
   if (mykey < n) {
     const int64_t roff = hoff + (int64_t)mykey * sl;
 #pragma unroll
@@ -278,14 +324,18 @@ void dkdv_kernel(const KArgs a) {
   }
 }
 
-template <int D, int CPT, bool C, bool G, bool SP>
+template <int D, int CPT, bool C, bool G, bool SP, bool DG = false>
 static hipError_t launch_one(const KArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((dkdv_kernel<D, CPT, C, G, SP>), dim3(a.nitems), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((dkdv_kernel<D, CPT, C, G, SP, DG>), dim3(a.nitems), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D, int CPT>
 static hipError_t dispatch(const KArgs& a, bool c, bool g, bool sp, hipStream_t st) {
+  if (a.aux) {   // gate gradient (gated only)
+    if (c) return sp ? launch_one<D, CPT, true, true, true, true>(a, st) : launch_one<D, CPT, true, true, false, true>(a, st);
+    return sp ? launch_one<D, CPT, false, true, true, true>(a, st) : launch_one<D, CPT, false, true, false, true>(a, st);
+  }
   if (c) {
     if (g) return sp ? launch_one<D, CPT, true, true, true>(a, st) : launch_one<D, CPT, true, true, false>(a, st);
     return sp ? launch_one<D, CPT, true, false, true>(a, st) : launch_one<D, CPT, true, false, false>(a, st);

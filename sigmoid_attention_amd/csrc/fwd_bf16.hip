@@ -21,6 +21,12 @@
 // the valid length, or cross the wave's diagonal under the causal rule, zero the pairs
 // with key >= n or key > query. With a gate, a per-key table in LDS supplies the logit
 // offset (+inf for padded or dropped keys, which makes P exactly 0) and value factor.
+//
+// With RS the pass also writes the row mass sum_j P_ij of every valid query (the
+// row-sum diagnostic of "Sigmoid Attention as a Better Substrate for Learned KV Cache
+// Eviction": without row normalisation the total weight of a row is free). Each lane
+// adds the masked weights of its query column before the value gate is applied; the
+// two lanes holding one query are combined in the epilogue.
 #include <type_traits>
 
 #include "common.h"
@@ -56,7 +62,7 @@ struct FwdOcc {
   static constexpr int value = 2;
 };
 
-template <int D, int QB, int CPT, bool CAUSAL, bool GATED, bool SPLIT>
+template <int D, int QB, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool RS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<D, QB>::value, FwdOcc<D, QB>::value)))
 void fwd_kernel(const KArgs a) {
   using T = FwdTraits<D, QB, CPT, GATED>;
@@ -132,6 +138,9 @@ void fwd_kernel(const KArgs a) {
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) acc[qb][dt] = zero16();
+  float mass[QB];   // RS: sum of this lane's weights per query block
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mass[qb] = 0.0f;
 
   wait_vmem_and_barrier();
 
@@ -165,14 +174,17 @@ void fwd_kernel(const KArgs a) {
       const int ld = q0 + 32 * qb + (l & 31) - kb - lk;
       lim = ld < lim ? ld : lim;
     }
+    float part = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = r0 + e;
       float x = sigmoid_l2(s_cur[r], c1, GATED ? tc2[e] : c2);
-      if (GATED) x *= tg[e];
       if (MODE == kMasked) x = arc(r) <= lim ? x : 0.0f;
+      if (RS) part += x;
+      if (GATED) x *= tg[e];
       p[r] = x;
     }
+    if (RS) mass[qb] += part;
   };
   auto to_bf16 = [&](const f32x16& p, int h, bf16x8& ph, bf16x8& pl) {
     if (SPLIT) split8(p, 8 * h, ph, pl, sel);
@@ -304,6 +316,14 @@ void fwd_kernel(const KArgs a) {
   for (int dt = 0; dt < T::DT; ++dt) pv(dqb, dt, dvop[dt], dph, dpl);
 
   // epilogue: valid query rows only (rows >= n are zero-filled by a separate kernel)
+  if (RS) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      mass[qb] += __shfl_xor(mass[qb], 32, 64);
+      const int query = q0 + 32 * qb + (l & 31);
+      if (l < 32 && query < n) a.aux[((int64_t)it.b * a.H + it.h) * a.Lmax + query] = mass[qb];
+    }
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int query = q0 + 32 * qb + (l & 31);
@@ -315,20 +335,25 @@ void fwd_kernel(const KArgs a) {
   }
 }
 
-template <int D, int QB, int CPT, bool C, bool G, bool SP>
+template <int D, int QB, int CPT, bool C, bool G, bool SP, bool RS>
 static hipError_t launch_one(const KArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP>), dim3(a.nitems), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP, RS>), dim3(a.nitems), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <int D, int QB, int CPT, bool RS>
+static hipError_t dispatch_rs(const KArgs& a, bool c, bool g, bool sp, hipStream_t st) {
+  if (c) {
+    if (g) return sp ? launch_one<D, QB, CPT, true, true, true, RS>(a, st) : launch_one<D, QB, CPT, true, true, false, RS>(a, st);
+    return sp ? launch_one<D, QB, CPT, true, false, true, RS>(a, st) : launch_one<D, QB, CPT, true, false, false, RS>(a, st);
+  }
+  if (g) return sp ? launch_one<D, QB, CPT, false, true, true, RS>(a, st) : launch_one<D, QB, CPT, false, true, false, RS>(a, st);
+  return sp ? launch_one<D, QB, CPT, false, false, true, RS>(a, st) : launch_one<D, QB, CPT, false, false, false, RS>(a, st);
 }
 
 template <int D, int QB, int CPT>
 static hipError_t dispatch(const KArgs& a, bool c, bool g, bool sp, hipStream_t st) {
-  if (c) {
-    if (g) return sp ? launch_one<D, QB, CPT, true, true, true>(a, st) : launch_one<D, QB, CPT, true, true, false>(a, st);
-    return sp ? launch_one<D, QB, CPT, true, false, true>(a, st) : launch_one<D, QB, CPT, true, false, false>(a, st);
-  }
-  if (g) return sp ? launch_one<D, QB, CPT, false, true, true>(a, st) : launch_one<D, QB, CPT, false, true, false>(a, st);
-  return sp ? launch_one<D, QB, CPT, false, false, true>(a, st) : launch_one<D, QB, CPT, false, false, false>(a, st);
+  return a.aux ? dispatch_rs<D, QB, CPT, true>(a, c, g, sp, st) : dispatch_rs<D, QB, CPT, false>(a, c, g, sp, st);
 }
 
 int fwd_tile_rows(int d) { return d == 64 ? FwdTraits<64, SA_FWD64_QB, 2, false>::BM : FwdTraits<128, 1, 1, false>::BM; }

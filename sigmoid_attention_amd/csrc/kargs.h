@@ -30,6 +30,8 @@ struct KArgs {
   const void* dout;
   void* out0;            // o (fwd), dq (dq pass), dk (dk/dv pass)
   void* out1;            // dv (dk/dv pass)
+  float* aux;            // per-head float plane [B][H][Lmax] or null: dg (dk/dv pass),
+                         // row mass (forward)
   const float* gate;     // [B][gsb] device floats or null
   int64_t sb, sh, sl;    // element strides of the 4-D tensors
   int64_t gsb;           // gate batch stride (elements)

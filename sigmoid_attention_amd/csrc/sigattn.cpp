@@ -24,6 +24,7 @@ int fwd_tile_rows(int d);
 int dq_tile_rows(int d);
 int dkdv_tile_rows(int d);
 hipError_t launch_zero_rows(const ZArgs& z, int B, int H, hipStream_t st);
+hipError_t launch_plane_tail(const PArgs& pa, hipStream_t st);
 hipError_t launch_f32(const DArgs& a, int pass, hipStream_t st);
 }  // namespace sa
 
@@ -175,11 +176,26 @@ sigattn_status zero_fill(const sigattn_problem* p, void* o0, void* o1, hipStream
   return sa::launch_zero_rows(z, p->B, p->H, st) == hipSuccess ? SIGATTN_OK : SIGATTN_ERR_HIP;
 }
 
+// Zero the padded entries of a per-head float plane and, if `sum` is set, reduce it over
+// heads; enqueued after the pass that wrote the valid entries.
+sigattn_status plane_tail(const sigattn_problem* p, float* plane, float* sum, hipStream_t st) {
+  sa::PArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  pa.plane = plane;
+  pa.sum = sum;
+  pa.B = p->B;
+  pa.H = p->H;
+  pa.Lmax = p->Lmax;
+  for (int b = 0; b < p->B; ++b) pa.len[b] = (uint16_t)p->seqlens[b];
+  return sa::launch_plane_tail(pa, st) == hipSuccess ? SIGATTN_OK : SIGATTN_ERR_HIP;
+}
+
 sigattn_status run_f32(const sigattn_problem* p, int pass, const void* q, const void* k,
-                       const void* v, const void* dout, void* o0, void* o1, hipStream_t st) {
+                       const void* v, const void* dout, void* o0, void* o1, float* aux,
+                       hipStream_t st) {
   sa::DArgs a;
   std::memset(&a, 0, sizeof(a));
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1; a.aux = aux;
   a.gate = p->gate;
   a.sb = p->stride_b; a.sh = p->stride_h; a.sl = p->stride_l;
   a.gsb = p->gate_stride_b ? p->gate_stride_b : p->Lmax;
@@ -197,14 +213,22 @@ sigattn_status run_f32(const sigattn_problem* p, int pass, const void* q, const 
   return zero_fill(p, o0, o1, st);
 }
 
+// aux: the per-head float plane of the pass (row mass for the forward, gate gradient for
+// the dk/dv pass) or null; aux_sum: its sum over heads or null.
 sigattn_status run_pass(const sigattn_problem* p, int pass, const void* q, const void* k,
-                        const void* v, const void* dout, void* o0, void* o1, void* stream) {
+                        const void* v, const void* dout, void* o0, void* o1, void* stream,
+                        float* aux = nullptr, float* aux_sum = nullptr) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (p->B == 0) return SIGATTN_OK;
-  if (p->dtype == SIGATTN_F32) return run_f32(p, pass, q, k, v, dout, o0, o1, st);
+  sigattn_status s;
+  if (p->dtype == SIGATTN_F32) {
+    s = run_f32(p, pass, q, k, v, dout, o0, o1, aux, st);
+    if (s != SIGATTN_OK || !aux) return s;
+    return plane_tail(p, aux, aux_sum, st);
+  }
   KArgs a;
   plan_pass(p, pass, &a);
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1; a.aux = aux;
   const bool causal = p->causal != 0, gated = p->gate != nullptr;
   if (a.nitems > 0) {
     hipError_t e;
@@ -214,7 +238,17 @@ sigattn_status run_pass(const sigattn_problem* p, int pass, const void* q, const
     else e = sa::launch_dkdv_bf16(a, p->d, causal, gated, split, st);
     if (e != hipSuccess) return SIGATTN_ERR_HIP;
   }
-  return zero_fill(p, o0, o1, st);
+  if ((s = zero_fill(p, o0, o1, st)) != SIGATTN_OK || !aux) return s;
+  return plane_tail(p, aux, aux_sum, st);
+}
+
+// A per-head float plane or its head sum: 4-byte aligned, distinct from every tensor.
+sigattn_status check_plane(const void* plane, const void* const* others, int nothers) {
+  if (!plane) return SIGATTN_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(plane) & 3u) return SIGATTN_ERR_ALIGNMENT;
+  for (int i = 0; i < nothers; ++i)
+    if (others[i] == plane) return SIGATTN_ERR_INVALID_ARG;
+  return SIGATTN_OK;
 }
 
 }  // namespace
@@ -231,6 +265,18 @@ sigattn_status sigattn_fwd(const sigattn_problem* p, const void* q, const void* 
   void* out[1] = {o};
   if ((s = check_tensors(in, 3, out, 1)) != SIGATTN_OK) return s;
   return run_pass(p, 0, q, k, v, nullptr, o, nullptr, stream);
+}
+
+sigattn_status sigattn_fwd_rowsum(const sigattn_problem* p, const void* q, const void* k,
+                                  const void* v, void* o, float* row_mass, void* stream) {
+  sigattn_status s = validate_problem(p);
+  if (s != SIGATTN_OK) return s;
+  const void* in[3] = {q, k, v};
+  void* out[1] = {o};
+  if ((s = check_tensors(in, 3, out, 1)) != SIGATTN_OK) return s;
+  const void* others[5] = {q, k, v, o, p->gate};
+  if ((s = check_plane(row_mass, others, 5)) != SIGATTN_OK) return s;
+  return run_pass(p, 0, q, k, v, nullptr, o, nullptr, stream, row_mass, nullptr);
 }
 
 sigattn_status sigattn_bwd_dq(const sigattn_problem* p, const void* q, const void* k,
@@ -252,6 +298,24 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_problem* p, const void* q, const v
   void* out[2] = {dk, dv};
   if ((s = check_tensors(in, 4, out, 2)) != SIGATTN_OK) return s;
   return run_pass(p, 2, q, k, v, dout, dk, dv, stream);
+}
+
+sigattn_status sigattn_bwd_dkdv_dg(const sigattn_problem* p, const void* q, const void* k,
+                                   const void* v, const void* dout, void* dk, void* dv,
+                                   float* dg_head, float* dg, void* stream) {
+  sigattn_status s = validate_problem(p);
+  if (s != SIGATTN_OK) return s;
+  if (!p->gate) return SIGATTN_ERR_INVALID_ARG;
+  const void* in[4] = {q, k, v, dout};
+  void* out[2] = {dk, dv};
+  if ((s = check_tensors(in, 4, out, 2)) != SIGATTN_OK) return s;
+  const void* others[7] = {q, k, v, dout, dk, dv, p->gate};
+  if ((s = check_plane(dg_head, others, 7)) != SIGATTN_OK) return s;
+  if (dg) {
+    const void* others2[8] = {q, k, v, dout, dk, dv, p->gate, dg_head};
+    if ((s = check_plane(dg, others2, 8)) != SIGATTN_OK) return s;
+  }
+  return run_pass(p, 2, q, k, v, dout, dk, dv, stream, dg_head, dg);
 }
 
 int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int64_t cap,

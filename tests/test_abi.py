@@ -174,3 +174,24 @@ def test_plan_xcd_grouping_keeps_heads_together(lib):
     items, tile = S.plan(p, 0)
     xcd0 = items[0::8][:16]
     assert len({(b, h) for b, h, t in xcd0.tolist()}) <= 2
+
+
+def test_gate_gradient_entry_rejects_before_launch(lib):
+    """sigattn_bwd_dkdv_dg needs a gate and a distinct, 4-byte aligned dg_head plane;
+    every error is returned before anything is enqueued (fake pointers)."""
+    vp = ctypes.c_void_p
+    q, dk, dv, dgh, dg = (vp((1 << 20) * (i + 1)) for i in range(5))
+    p, keep = _prob()
+    f = lib.sigattn_bwd_dkdv_dg
+    # no gate
+    assert f(ctypes.byref(p), q, q, q, q, dk, dv, dgh, dg, None) == 1
+    p, keep = _prob(gate_ptr=1 << 26)
+    # missing dg_head
+    assert f(ctypes.byref(p), q, q, q, q, dk, dv, None, dg, None) == 1
+    # dg_head misaligned, or aliasing dk, or dg aliasing dg_head
+    assert f(ctypes.byref(p), q, q, q, q, dk, dv, vp((1 << 23) + 2), dg, None) == 3
+    assert f(ctypes.byref(p), q, q, q, q, dk, dv, dk, dg, None) == 1
+    assert f(ctypes.byref(p), q, q, q, q, dk, dv, dgh, dgh, None) == 1
+    # a bad problem is still reported first
+    p.d = 96
+    assert f(ctypes.byref(p), q, q, q, q, dk, dv, dgh, dg, None) == 2

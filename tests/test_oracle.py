@@ -596,3 +596,21 @@ def test_row_mass_is_forward_with_unit_values():
         o = O.forward(q, k, np.ones((B, H, L, d)), seqlens, causal=causal)
         for c in range(d):
             np.testing.assert_allclose(R, o[..., c], rtol=1e-13, atol=0)
+
+
+def test_gate_grad_absolute_sums():
+    """The magnitude sums of the gate gradient equal it when every term is non-negative
+    and bound it otherwise."""
+    B, H, L, d = 2, 2, 12, 4
+    seqlens = [12, 7]
+    rng = np.random.default_rng(181)
+    q, k, v, do = (rng.standard_normal((B, H, L, d)) for _ in range(4))
+    g = rng.uniform(0.1, 1.0, (B, L))
+    # dO . v_j >= 0 and sigma' > 0 make every term non-negative
+    pos = [np.abs(t) for t in (q, k, v, do)]
+    a, _ = O.gate_grad(*pos, seqlens, g, causal=True)
+    m, _ = O.gate_grad(*pos, seqlens, g, causal=True, absolute=True)
+    np.testing.assert_allclose(a, m, rtol=1e-12, atol=1e-15)
+    a, _ = O.gate_grad(q, k, v, do, seqlens, g)
+    m, _ = O.gate_grad(q, k, v, do, seqlens, g, absolute=True)
+    assert np.all(np.abs(a) <= m + 1e-12)
