@@ -41,6 +41,16 @@ Readings taken where the pages are silent (each is also listed in the design not
   dg_j = sum_i dS_ij / (g_j + eps) + v_j . sum_i P_ij dO_i, per head; the gate is shared
   by the heads, so the gradient of the shared gate is the sum over heads. The hard drop
   is a step function of g: a dropped key gets derivative 0, like a padded key.
+* Decode with eviction ([KV-evict] gate paragraphs): after prefill the entries with
+  g_j < tau (j >= sink) are physically removed; each entry written during decode is kept
+  or removed by the same rule when it is written; kept entries keep their log-gate on
+  the logits and their gate factor on the values. The cache holds the kept entries in
+  position order. A decode step writes the new token's entry first and then lets the
+  new query attend to the whole cache, so a dropped new entry is not seen even by its
+  own query (as a dropped key is masked for every query in the forward). The bias of a
+  decode step is an input (the model's beta, e.g. -log n of the sequence length it was
+  trained with); with it, decoding query i against the cache of tokens 0..i gives row i
+  of the causal forward with hard dropping.
 * Row mass ([KV-evict] row-sum diagnostic): sum_j P_ij over the allowed keys of query
   i, i.e. the sum of the attention weights of the row, with the gate's log term in the
   logits but without the value factor g_j. Padded rows give 0.
@@ -75,6 +85,9 @@ __all__ = [
     "gate_grad",
     "gate_grad_rows",
     "row_mass",
+    "cache_compact",
+    "cache_append",
+    "decode",
     "forward_naive",
     "backward_naive",
 ]
@@ -417,6 +430,89 @@ def row_mass(q, k, seqlens, causal=False, gate=None, tau=0.0, sink=DEFAULT_SINK,
                 P = _P(q[b, h, rows], k[b, h, :n], rows, cols, s, beta, logg, keep, causal)
                 R[b, h, rows] = P.sum(axis=1)
     return R
+
+
+# ----------------------------------------------------------------------------------
+# decode against a KV cache with threshold eviction
+# ----------------------------------------------------------------------------------
+
+def cache_compact(k, v, seqlens, cap, gate=None, tau=0.0, sink=DEFAULT_SINK):
+    """Cache built from a prefill ([KV-evict]: entries with g_j < tau are removed after
+    prefill, except the first `sink` positions): the kept keys of each sequence, in
+    position order, in slots 0..count_b-1 of a cache of `cap` slots.
+
+    k, v: [B, H, L, d]; gate: [B, L] or None (then every valid key is kept).
+    Returns (Kc [B, H, cap, d], Vc, Gc [B, cap] or None, count [B], seen [B]) with unused
+    slots 0 and seen_b = n_b (the number of positions written so far).
+    """
+    k, v = np.asarray(k), np.asarray(v)
+    B, H, L, d = k.shape
+    Kc, Vc = np.zeros((B, H, cap, d), k.dtype), np.zeros((B, H, cap, d), v.dtype)
+    Gc = None if gate is None else np.zeros((B, cap), np.asarray(gate).dtype)
+    count = np.zeros(B, np.int64)
+    seen = np.asarray(seqlens, np.int64).copy()
+    for b in range(B):
+        n = int(seqlens[b])
+        kept = np.nonzero(kept_keys(n, L, None if gate is None else gate[b], tau, sink))[0]
+        if len(kept) > cap:
+            raise ValueError("cache capacity exceeded")
+        m = len(kept)
+        Kc[b, :, :m] = k[b][:, kept]
+        Vc[b, :, :m] = v[b][:, kept]
+        if Gc is not None:
+            Gc[b, :m] = gate[b][kept]
+        count[b] = m
+    return Kc, Vc, Gc, count, seen
+
+
+def cache_append(Kc, Vc, Gc, count, seen, k_new, v_new, g_new=None, tau=0.0,
+                 sink=DEFAULT_SINK):
+    """One decode-time write ([KV-evict]: the threshold rule is applied to each newly
+    written entry): the new token of sequence b sits at position seen_b; it is kept iff
+    there is no gate, or seen_b < sink, or g_new_b >= tau. Kept entries go to slot
+    count_b. Returns new (Kc, Vc, Gc, count, seen); the inputs are not modified.
+
+    k_new, v_new: [B, H, d]; g_new: [B] or None.
+    """
+    Kc, Vc = Kc.copy(), Vc.copy()
+    Gc = None if Gc is None else Gc.copy()
+    count, seen = np.asarray(count).copy(), np.asarray(seen).copy()
+    cap = Kc.shape[2]
+    for b in range(Kc.shape[0]):
+        keep = g_new is None or tau <= 0.0 or seen[b] < sink or g_new[b] >= tau
+        if keep:
+            if count[b] >= cap:
+                raise ValueError("cache capacity exceeded")
+            Kc[b, :, count[b]] = k_new[b]
+            Vc[b, :, count[b]] = v_new[b]
+            if Gc is not None:
+                Gc[b, count[b]] = g_new[b]
+            count[b] += 1
+        seen[b] += 1
+    return Kc, Vc, Gc, count, seen
+
+
+def decode(q, Kc, Vc, Gc, count, bias, eps=GATE_EPS, scale=None):
+    """One query per (b, h) against the live cache entries j < count_b:
+        o = sum_j sigma(s q . k_j + beta_b [+ log(g_j + eps)]) [g_j] v_j
+    (section 3 equation of [SA-bio] with the gate injection of [KV-evict]).
+    q: [B, H, d]; bias: [B] (beta_b). Returns float64 [B, H, d]; count_b = 0 gives 0."""
+    q = _as64(q)
+    B, H, d = q.shape
+    s = _params(d, scale)
+    out = np.zeros((B, H, d))
+    for b in range(B):
+        m = int(count[b])
+        if m == 0:
+            continue
+        x = s * np.einsum("hc,hjc->hj", q[b], _as64(Kc[b, :, :m])) + float(bias[b])
+        vals = _as64(Vc[b, :, :m])
+        if Gc is not None:
+            g = _as64(Gc[b, :m])
+            x = x + np.log(g + eps)[None, :]
+            vals = vals * g[None, :, None]
+        out[b] = np.einsum("hj,hjc->hc", logistic(x), vals)
+    return out
 
 
 # ----------------------------------------------------------------------------------

@@ -614,3 +614,87 @@ def test_gate_grad_absolute_sums():
     a, _ = O.gate_grad(q, k, v, do, seqlens, g)
     m, _ = O.gate_grad(q, k, v, do, seqlens, g, absolute=True)
     assert np.all(np.abs(a) <= m + 1e-12)
+
+
+# ----------------------------------------------------------------------------------
+# decode against a KV cache with threshold eviction
+# ----------------------------------------------------------------------------------
+
+def _decode_case(seed, B=3, H=2, L=24, d=8):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    g = rng.uniform(0.0, 1.0, (B, L))
+    g[:, 7] = 0.01                      # a dropped key at a fixed position
+    g[:, 1] = 0.02                      # below tau but inside the sink: kept
+    return q, k, v, g
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_decode_matches_causal_forward_rows(gated):
+    """Decoding query i against the cache of tokens 0..i (prefill compaction of the first
+    p tokens, then one append per token) gives row i of the causal forward with hard
+    dropping, at the sequence's bias: the eviction rule of the KV-eviction paper applied
+    at prefill and to each newly written entry."""
+    q, k, v, g = _decode_case(120)
+    B, H, L, d = q.shape
+    tau, sink = (0.3, 4) if gated else (0.0, 4)
+    gate = g if gated else None
+    seqlens = [L] * B
+    bias = np.array([O.sequence_bias(L)] * B)
+    ref = O.forward(q, k, v, seqlens, causal=True, gate=gate, tau=tau, sink=sink, bias=bias)
+    p = 9
+    state = O.cache_compact(k[:, :, :p], v[:, :, :p], [p] * B, L, gate=None if gate is None else gate[:, :p],
+                            tau=tau, sink=sink)
+    for i in range(L):
+        if i >= p:
+            state = O.cache_append(*state, k[:, :, i], v[:, :, i],
+                                   None if gate is None else gate[:, i], tau=tau, sink=sink)
+        if i < p - 1:
+            # the cache of tokens 0..i, built by compaction of the prefix
+            st = O.cache_compact(k[:, :, :i + 1], v[:, :, :i + 1], [i + 1] * B, L,
+                                 gate=None if gate is None else gate[:, :i + 1], tau=tau, sink=sink)
+        else:
+            st = state
+        Kc, Vc, Gc, count, seen = st
+        assert np.all(seen == i + 1)
+        got = O.decode(q[:, :, i], Kc, Vc, Gc, count, bias)
+        np.testing.assert_allclose(got, ref[:, :, i], rtol=1e-12, atol=1e-14)
+
+
+def test_cache_appends_equal_compaction():
+    """Appending tokens one by one gives exactly the cache compaction of the whole
+    prefill (same slots, same values, same counts)."""
+    q, k, v, g = _decode_case(121)
+    B, H, L, d = k.shape
+    lens = [24, 10, 0]
+    full = O.cache_compact(k, v, lens, 32, gate=g, tau=0.3, sink=4)
+    st = O.cache_compact(k[:, :, :0], v[:, :, :0], [0] * B, 32, gate=g[:, :0], tau=0.3, sink=4)
+    for i in range(L):
+        nxt = O.cache_append(*st, k[:, :, i], v[:, :, i], g[:, i], tau=0.3, sink=4)
+        # sequences shorter than i + 1 tokens do not advance
+        keep_b = np.array([i < n for n in lens])
+        st = tuple(np.where(keep_b.reshape((-1,) + (1,) * (a.ndim - 1)), a, b_)
+                   if a is not None else None for a, b_ in zip(nxt, st))
+    for a, b_ in zip(st, full):
+        np.testing.assert_array_equal(a, b_)
+    kept0 = [j for j in range(24) if j < 4 or g[0, j] >= 0.3]
+    assert full[3][0] == len(kept0)
+    np.testing.assert_array_equal(full[0][0, :, :len(kept0)], k[0][:, kept0])
+
+
+def test_decode_closed_form_q_zero():
+    """q = 0: every logit is beta + log(g_j + eps); with beta = -ln n the weight is
+    (g_j + eps) / (n + g_j + eps), so o = sum_j g_j (g_j+eps)/(n+g_j+eps) v_j."""
+    rng = np.random.default_rng(122)
+    B, H, C, d = 2, 3, 10, 4
+    Kc, Vc = rng.standard_normal((B, H, C, d)), rng.standard_normal((B, H, C, d))
+    Gc = rng.uniform(0.05, 1.0, (B, C))
+    count = np.array([10, 6])
+    n = 40
+    out = O.decode(np.zeros((B, H, d)), Kc, Vc, Gc, count, [-math.log(n)] * B)
+    eps = O.GATE_EPS
+    for b in range(B):
+        m = count[b]
+        w = Gc[b, :m] * (Gc[b, :m] + eps) / (n + Gc[b, :m] + eps)
+        np.testing.assert_allclose(out[b], np.einsum("j,hjc->hc", w, Vc[b, :, :m]), rtol=1e-12)
+    assert np.all(O.decode(np.zeros((B, H, d)), Kc, Vc, Gc, np.array([0, 0]), [0.0, 0.0]) == 0)
