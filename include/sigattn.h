@@ -39,9 +39,10 @@
  *  - seqlens and bias are HOST arrays of length B, read during the call only.
  *    gate is a DEVICE array of floats, gate[b * gate_stride_b + j], j < Lmax.
  *  - The caller owns every buffer. The library never allocates, frees or
- *    synchronises; it needs no workspace. Work is enqueued on `stream` (a hipStream_t;
- *    NULL is the default stream) and the results are valid once that stream has
- *    completed it. Identical inputs give bitwise-identical outputs (no atomics).
+ *    synchronises; only sigattn_decode needs a workspace, which the caller passes.
+ *    Work is enqueued on `stream` (a hipStream_t; NULL is the default stream) and the
+ *    results are valid once that stream has completed it. Identical inputs give
+ *    bitwise-identical outputs (no atomics).
  *  - Outputs are fully written: rows i >= n of O and dQ, rows j >= n of dK and dV,
  *    and the dK/dV rows of dropped keys are exactly 0. Values in padded input slots
  *    are never read. Inputs are not modified; outputs must not alias inputs.
@@ -142,6 +143,75 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_problem* p, const void* q, const v
 sigattn_status sigattn_bwd_dkdv_dg(const sigattn_problem* p, const void* q, const void* k,
                                    const void* v, const void* dout, void* dk, void* dv,
                                    float* dg_head, float* dg, void* stream);
+
+/* ------------------- KV cache with threshold eviction, single-query decode -------------------
+ *
+ * "Sigmoid Attention as a Better Substrate for Learned KV Cache Eviction", gate paragraphs:
+ * at inference the soft gate becomes physical deletion. After prefill, entries with
+ * g_j < gate_tau are removed; every entry written during decode is kept or removed by the
+ * same rule when it is written; positions below gate_sink are never removed; kept entries
+ * keep log(g_j + eps) on their logits and g_j on their values. A cache holds only kept
+ * entries, in position order, in slots 0..count_b-1; slots at or past count_b hold
+ * unspecified values and are never read. The counters live in device memory and are
+ * updated by the kernels, so no gate value ever has to travel to the host.
+ *
+ * A decode step for a new token: write its entry with sigattn_cache_append (kept or not
+ * by the rule), then sigattn_decode lets its query attend to the whole cache; a dropped
+ * new entry is therefore not seen even by its own query, exactly as a dropped key is
+ * masked for every query of the forward. With the bias of the forward, decoding query i
+ * against the cache of tokens 0..i reproduces row i of the causal forward.
+ */
+typedef struct sigattn_cache {
+  uint32_t struct_size;          /* sizeof(sigattn_cache): ABI check */
+  int32_t B, H, d, cap;          /* 0 <= B <= 256, H >= 1, d in {64,128}, 1 <= cap <= 2^24 */
+  int64_t stride_b, stride_h, stride_l;  /* element strides of k and v; d <= stride_l <= 2^22 */
+  void* k;                       /* DEVICE bf16 [B][H][cap][d] cached keys */
+  void* v;                       /* DEVICE bf16 [B][H][cap][d] cached values */
+  float* gate;                   /* DEVICE float [B][cap] gates of the cached entries, or NULL
+                                    for a cache without gates (nothing is ever removed) */
+  int32_t* count;                /* DEVICE int32 [B]: live entries per sequence */
+  int32_t* seen;                 /* DEVICE int32 [B]: positions written so far */
+  float gate_eps;                /* eps inside log(g + eps), >= 0 (1e-8 in the pages) */
+  float gate_tau;                /* removal threshold, >= 0 (0.05 in the pages; 0 keeps all) */
+  int32_t gate_sink;             /* leading positions never removed (4 in the pages) */
+} sigattn_cache;
+
+/* Build a cache from a prefill: the kept rows of k and v ([B][H][Lmax][d] bf16 described
+ * by p: shapes, strides, seqlens; p->gate and p->gate_stride_b give the gates) are copied
+ * to slots 0.. in position order, with their gates; count_b = number kept, seen_b = n_b.
+ * The removal rule is the cache's (c->gate_tau, c->gate_sink); p's gate_tau, gate_sink
+ * and gate_eps are not used. Requires p->dtype bf16, c->B == p->B, c->H == p->H,
+ * c->d == p->d, c->cap >= every n_b, and c->gate != NULL exactly when p->gate != NULL. */
+sigattn_status sigattn_cache_build(const sigattn_cache* c, const sigattn_problem* p,
+                                   const void* k, const void* v, void* stream);
+
+/* Write one new entry per sequence: k_new, v_new are DEVICE bf16 [B][H][d] with element
+ * strides (stride_b, stride_h), rows 16-byte aligned; g_new is DEVICE float [B] (required
+ * when the cache has gates, else must be NULL). The entry of sequence b, at position
+ * seen_b, is kept iff the cache has no gates, gate_tau == 0, seen_b < gate_sink, or
+ * g_new_b >= gate_tau; a kept entry goes to slot count_b. seen_b always advances. If a
+ * kept entry finds its cache full (count_b == cap) it is not stored and, when status is
+ * not NULL, the DEVICE int32 *status is set to 1 (it is never cleared by the library). */
+sigattn_status sigattn_cache_append(const sigattn_cache* c, const void* k_new,
+                                    const void* v_new, int64_t stride_b, int64_t stride_h,
+                                    const float* g_new, int32_t* status, void* stream);
+
+/* Bytes of device workspace sigattn_decode needs for this cache (the per-chunk partial
+ * sums: B * H * ceil(cap / 512) * d floats), or -1 if the cache description is invalid. */
+int64_t sigattn_decode_workspace_size(const sigattn_cache* c);
+
+/* Single-query decode: o_bh = sum_{j < count_b} sigma(s q_bh . k_j + beta_b
+ * [+ log(g_j + eps)]) [g_j] v_j (section 3 equation with the gate injection). q is DEVICE
+ * bf16 [B][H][d] with element strides (stride_b, stride_h) (16-byte aligned rows); o has
+ * the same strides, in out_dtype (SIGATTN_BF16 or SIGATTN_F32); count_b = 0 gives 0.
+ * bias is a HOST float [B] array, required: beta_b, the bias the model uses for that
+ * sequence (the pages' -log n). scale 0 selects 1/sqrt(d). workspace: DEVICE, at least
+ * sigattn_decode_workspace_size(c) bytes, 16-byte aligned, owned by the caller; calls
+ * that share a workspace must not overlap in time. Must not alias any other argument. */
+sigattn_status sigattn_decode(const sigattn_cache* c, const void* q, int64_t stride_b,
+                              int64_t stride_h, const float* bias, float scale, void* o,
+                              int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+                              void* stream);
 
 /* Host-side view of the work list a pass launches, for inspection and tests.
  * pass: 0 forward, 1 dq, 2 dk/dv. Writes up to `cap` items as (b, h, tile) int32

@@ -11,6 +11,8 @@ raises, there is no fallback.
     dq = bwd_dq(q, k, v, do, seqlens, ...)
     dk, dv = bwd_dkdv(q, k, v, do, seqlens, ...)
     dk, dv, dg_head, dg = bwd_dkdv_dg(q, k, v, do, seqlens, gate=g, ...)
+    cache = KVCache(B, H, d, cap, gated=True, tau=0.05)   # KV cache with eviction
+    cache.build(k, v, seqlens, gate=g); cache.append(k1, v1, g1); o1 = cache.decode(q1, bias)
 
 Tensors are [B, H, Lmax, d] views (any strides with a contiguous last dimension, the
 same strides for all of them), bf16 or float32 (the float32 debug path), on one GPU.
@@ -25,7 +27,8 @@ import os
 
 import numpy as np
 
-__all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd_dkdv_dg", "validate", "plan", "library_path", "load",
+__all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd_dkdv_dg", "KVCache", "CacheDesc",
+           "validate", "plan", "library_path", "load",
            "Problem", "SigattnError", "STATUS", "VERSION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +69,21 @@ class Problem(ctypes.Structure):
     ]
 
 
+class CacheDesc(ctypes.Structure):
+    """Mirror of ``sigattn_cache`` in include/sigattn.h."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("cap", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+        ("stride_l", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+        ("count", ctypes.c_void_p), ("seen", ctypes.c_void_p),
+        ("gate_eps", ctypes.c_float), ("gate_tau", ctypes.c_float),
+        ("gate_sink", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -89,6 +107,16 @@ def load():
     lib.sigattn_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dkdv_dg.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    C = ctypes.POINTER(CacheDesc)
+    i64 = ctypes.c_int64
+    lib.sigattn_cache_build.argtypes = [C, P, vp, vp, vp]
+    lib.sigattn_cache_append.argtypes = [C, vp, vp, i64, i64, vp, vp, vp]
+    lib.sigattn_decode_workspace_size.argtypes = [C]
+    lib.sigattn_decode_workspace_size.restype = i64
+    lib.sigattn_decode.argtypes = [C, vp, i64, i64, ctypes.POINTER(ctypes.c_float), ctypes.c_float,
+                                   vp, ctypes.c_int32, vp, i64, vp]
+    for f in (lib.sigattn_cache_build, lib.sigattn_cache_append, lib.sigattn_decode):
+        f.restype = ctypes.c_int
     lib.sigattn_plan.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                  ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]
     lib.sigattn_plan.restype = ctypes.c_int64
@@ -336,3 +364,87 @@ def fwd_rowsum(q, k, v, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, ep
     del keep
     _check(code, "sigattn_fwd_rowsum")
     return out, row_mass
+
+
+class KVCache:
+    """A KV cache with threshold eviction on one GPU (see sigattn_cache in the header):
+    keys and values [B, H, cap, d] bf16, gates [B, cap] float32 (when gated), and the
+    device counters count [B] (live entries) and seen [B] (positions written)."""
+
+    def __init__(self, B, H, d, cap, *, gated, eps=1e-8, tau=0.0, sink=4, device=None):
+        torch = _torch()
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        self.k = torch.zeros((B, H, cap, d), dtype=torch.bfloat16, device=dev)
+        self.v = torch.zeros_like(self.k)
+        self.gate = torch.zeros((B, cap), dtype=torch.float32, device=dev) if gated else None
+        self.count = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.seen = torch.zeros(B, dtype=torch.int32, device=dev)
+        c = CacheDesc()
+        c.struct_size = ctypes.sizeof(CacheDesc)
+        c.B, c.H, c.d, c.cap = B, H, d, cap
+        c.stride_b, c.stride_h, c.stride_l = self.k.stride()[:3]
+        c.k, c.v = self.k.data_ptr(), self.v.data_ptr()
+        c.gate = None if self.gate is None else self.gate.data_ptr()
+        c.count, c.seen = self.count.data_ptr(), self.seen.data_ptr()
+        c.gate_eps, c.gate_tau, c.gate_sink = float(eps), float(tau), int(sink)
+        self.desc = c
+        self.shape = (B, H, d, cap)
+
+    def _new_rows_ok(self, t, name):
+        torch = _torch()
+        B, H, d, _ = self.shape
+        if (tuple(t.shape) != (B, H, d) or t.dtype != torch.bfloat16 or t.device != self.k.device
+                or t.stride(-1) != 1):
+            raise ValueError(f"{name} must be a bf16 [B, H, d] tensor on the cache's GPU "
+                             "with a contiguous last dimension")
+
+    def build(self, k, v, seqlens, gate=None):
+        """Fill the cache from a prefill (k, v: [B, H, Lmax, d] bf16): kept rows only."""
+        lib = load()
+        prob, keep = _describe(k, (v,), seqlens, False, gate, 0.0, 0, 1e-8, 0.0, None)
+        code = lib.sigattn_cache_build(ctypes.byref(self.desc), ctypes.byref(prob),
+                                       k.data_ptr(), v.data_ptr(), _stream(k))
+        del keep
+        _check(code, "sigattn_cache_build")
+
+    def append(self, k_new, v_new, g_new=None, status=None):
+        """Write one new entry per sequence, kept or removed by the threshold rule."""
+        self._new_rows_ok(k_new, "k_new")
+        self._new_rows_ok(v_new, "v_new")
+        if k_new.stride() != v_new.stride():
+            raise ValueError("k_new and v_new must share strides")
+        lib = load()
+        code = lib.sigattn_cache_append(
+            ctypes.byref(self.desc), k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0),
+            k_new.stride(1), None if g_new is None else g_new.data_ptr(),
+            None if status is None else status.data_ptr(), _stream(k_new))
+        _check(code, "sigattn_cache_append")
+
+    def workspace_size(self) -> int:
+        return int(load().sigattn_decode_workspace_size(ctypes.byref(self.desc)))
+
+    def decode(self, q, bias, *, scale=0.0, out=None, out_dtype=None, workspace=None):
+        """o[b, h] = sum over live entries of sigma(s q.k + beta_b [+ log(g+eps)]) [g] v.
+        bias: host sequence of B floats (beta_b)."""
+        torch = _torch()
+        self._new_rows_ok(q, "q")
+        lib = load()
+        B = self.shape[0]
+        bb = np.ascontiguousarray(np.asarray(bias, dtype=np.float32).reshape(-1))
+        if bb.shape[0] != B:
+            raise ValueError("bias needs one value per sequence")
+        odt = torch.bfloat16 if out_dtype is None else out_dtype
+        if out is None:
+            out = torch.empty_strided(q.shape, q.stride(), dtype=odt, device=q.device)
+        if out.shape != q.shape or out.stride() != q.stride() or out.dtype != odt:
+            raise ValueError("out must match q in shape and strides, with the output dtype")
+        code_dt = F32 if odt == torch.float32 else BF16
+        if workspace is None:
+            workspace = torch.empty(max(1, (self.workspace_size() + 3) // 4),
+                                    dtype=torch.float32, device=q.device)
+        code = lib.sigattn_decode(ctypes.byref(self.desc), q.data_ptr(), q.stride(0),
+                                  q.stride(1), bb.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                  float(scale), out.data_ptr(), code_dt, workspace.data_ptr(),
+                                  workspace.numel() * 4, _stream(q))
+        _check(code, "sigattn_decode")
+        return out

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "aux_args.h"
+#include "dec_args.h"
 #include "kargs.h"
 
 namespace sa {
@@ -26,6 +27,9 @@ int dkdv_tile_rows(int d);
 hipError_t launch_zero_rows(const ZArgs& z, int B, int H, hipStream_t st);
 hipError_t launch_plane_tail(const PArgs& pa, hipStream_t st);
 hipError_t launch_f32(const DArgs& a, int pass, hipStream_t st);
+hipError_t launch_cache_build(const BuildArgs& a, int B, hipStream_t st);
+hipError_t launch_cache_append(const AppendArgs& a, int B, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 }  // namespace sa
 
 namespace {
@@ -251,6 +255,63 @@ sigattn_status check_plane(const void* plane, const void* const* others, int not
   return SIGATTN_OK;
 }
 
+// ------------------------------------ KV cache ------------------------------------
+
+constexpr int64_t kMaxCacheCap = int64_t(1) << 24;
+
+sigattn_status validate_cache(const sigattn_cache* c) {
+  if (!c) return SIGATTN_ERR_INVALID_ARG;
+  if (c->struct_size != sizeof(sigattn_cache)) return SIGATTN_ERR_INVALID_ARG;
+  if (c->B < 0 || c->H < 1 || c->cap < 1) return SIGATTN_ERR_INVALID_ARG;
+  if (c->B > SIGATTN_MAX_BATCH || c->cap > kMaxCacheCap) return SIGATTN_ERR_UNSUPPORTED;
+  if (c->d != 64 && c->d != 128) return SIGATTN_ERR_UNSUPPORTED;
+  if (c->stride_b < 0 || c->stride_h < 0 || c->stride_l < c->d) return SIGATTN_ERR_INVALID_ARG;
+  if (c->stride_l > SIGATTN_MAX_ROW_STRIDE) return SIGATTN_ERR_UNSUPPORTED;
+  if (((c->stride_l * 2) & 15) || ((c->stride_h * 2) & 15) || ((c->stride_b * 2) & 15))
+    return SIGATTN_ERR_ALIGNMENT;
+  if (!c->k || !c->v || !c->count || !c->seen) return SIGATTN_ERR_INVALID_ARG;
+  if (!aligned16(c->k) || !aligned16(c->v)) return SIGATTN_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(c->count) & 3u) || (reinterpret_cast<uintptr_t>(c->seen) & 3u) ||
+      (reinterpret_cast<uintptr_t>(c->gate) & 3u))
+    return SIGATTN_ERR_ALIGNMENT;
+  if (c->k == c->v || c->count == c->seen) return SIGATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(c->gate_eps) || c->gate_eps < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(c->gate_tau) || c->gate_tau < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+  if (c->gate_sink < 0) return SIGATTN_ERR_INVALID_ARG;
+  return SIGATTN_OK;
+}
+
+sa::CacheView cache_view(const sigattn_cache* c) {
+  sa::CacheView v;
+  std::memset(&v, 0, sizeof(v));
+  v.k = c->k;
+  v.v = c->v;
+  v.gate = c->gate;
+  v.count = c->count;
+  v.seen = c->seen;
+  v.sb = c->stride_b;
+  v.sh = c->stride_h;
+  v.sl = c->stride_l;
+  v.H = c->H;
+  v.cap = c->cap;
+  v.d = c->d;
+  v.gate_eps = c->gate_eps;
+  v.gate_tau = c->gate_tau;
+  v.gate_sink = c->gate_sink;
+  return v;
+}
+
+int64_t decode_chunks(const sigattn_cache* c) { return (c->cap + sa::kDecChunk - 1) / sa::kDecChunk; }
+
+int64_t decode_ws_bytes(const sigattn_cache* c) {
+  return (int64_t)c->B * c->H * decode_chunks(c) * c->d * (int64_t)sizeof(float);
+}
+
+// q/o rows ([B][H][d] with element strides sb, sh) must start on 16-byte boundaries
+bool rows16(int64_t sb, int64_t sh, int esize) {
+  return sb >= 0 && sh >= 0 && ((sb * esize) & 15) == 0 && ((sh * esize) & 15) == 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -316,6 +377,117 @@ sigattn_status sigattn_bwd_dkdv_dg(const sigattn_problem* p, const void* q, cons
     if ((s = check_plane(dg, others2, 8)) != SIGATTN_OK) return s;
   }
   return run_pass(p, 2, q, k, v, dout, dk, dv, stream, dg_head, dg);
+}
+
+sigattn_status sigattn_cache_build(const sigattn_cache* c, const sigattn_problem* p,
+                                   const void* k, const void* v, void* stream) {
+  sigattn_status s = validate_cache(c);
+  if (s != SIGATTN_OK) return s;
+  if ((s = validate_problem(p)) != SIGATTN_OK) return s;
+  if (p->dtype != SIGATTN_BF16) return SIGATTN_ERR_UNSUPPORTED;
+  if (p->B != c->B || p->H != c->H || p->d != c->d) return SIGATTN_ERR_INVALID_ARG;
+  if ((p->gate == nullptr) != (c->gate == nullptr)) return SIGATTN_ERR_INVALID_ARG;
+  for (int b = 0; b < p->B; ++b)
+    if (p->seqlens[b] > c->cap) return SIGATTN_ERR_INVALID_ARG;
+  const void* in[2] = {k, v};
+  if (!k || !v) return SIGATTN_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v)) return SIGATTN_ERR_ALIGNMENT;
+  const void* outs[5] = {c->k, c->v, c->gate, c->count, c->seen};
+  for (const void* i : in)
+    for (const void* o : outs)
+      if (o && i == o) return SIGATTN_ERR_INVALID_ARG;
+  if (p->B == 0) return SIGATTN_OK;
+  sa::BuildArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.c = cache_view(c);
+  a.k = k;
+  a.v = v;
+  a.gate = p->gate;
+  a.sb = p->stride_b;
+  a.sh = p->stride_h;
+  a.sl = p->stride_l;
+  a.gsb = p->gate_stride_b ? p->gate_stride_b : p->Lmax;
+  a.Lmax = p->Lmax;
+  for (int b = 0; b < p->B; ++b) a.len[b] = (uint16_t)p->seqlens[b];
+  return sa::launch_cache_build(a, p->B, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? SIGATTN_OK : SIGATTN_ERR_HIP;
+}
+
+sigattn_status sigattn_cache_append(const sigattn_cache* c, const void* k_new,
+                                    const void* v_new, int64_t stride_b, int64_t stride_h,
+                                    const float* g_new, int32_t* status, void* stream) {
+  sigattn_status s = validate_cache(c);
+  if (s != SIGATTN_OK) return s;
+  if (!k_new || !v_new || k_new == v_new) return SIGATTN_ERR_INVALID_ARG;
+  if ((g_new == nullptr) != (c->gate == nullptr)) return SIGATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !rows16(stride_b, stride_h, 2))
+    return SIGATTN_ERR_ALIGNMENT;
+  if ((reinterpret_cast<uintptr_t>(g_new) & 3u) || (reinterpret_cast<uintptr_t>(status) & 3u))
+    return SIGATTN_ERR_ALIGNMENT;
+  const void* outs[5] = {c->k, c->v, c->gate, c->count, c->seen};
+  for (const void* o : outs) {
+    if (!o) continue;
+    if (o == k_new || o == v_new || o == g_new || o == status) return SIGATTN_ERR_INVALID_ARG;
+  }
+  if (c->B == 0) return SIGATTN_OK;
+  sa::AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.c = cache_view(c);
+  a.k = k_new;
+  a.v = v_new;
+  a.gate = g_new;
+  a.nsb = stride_b;
+  a.nsh = stride_h;
+  a.status = status;
+  return sa::launch_cache_append(a, c->B, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? SIGATTN_OK : SIGATTN_ERR_HIP;
+}
+
+int64_t sigattn_decode_workspace_size(const sigattn_cache* c) {
+  if (validate_cache(c) != SIGATTN_OK) return -1;
+  return decode_ws_bytes(c);
+}
+
+sigattn_status sigattn_decode(const sigattn_cache* c, const void* q, int64_t stride_b,
+                              int64_t stride_h, const float* bias, float scale, void* o,
+                              int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  sigattn_status s = validate_cache(c);
+  if (s != SIGATTN_OK) return s;
+  if (out_dtype != SIGATTN_BF16 && out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || scale < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+  if (c->B > 0 && !bias) return SIGATTN_ERR_INVALID_ARG;
+  for (int b = 0; b < c->B; ++b)
+    if (!std::isfinite(bias[b])) return SIGATTN_ERR_INVALID_ARG;
+  if (!q || !o || !workspace) return SIGATTN_ERR_INVALID_ARG;
+  const int osize = out_dtype == SIGATTN_F32 ? 4 : 2;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(workspace) || !rows16(stride_b, stride_h, 2) ||
+      !rows16(stride_b, stride_h, osize))
+    return SIGATTN_ERR_ALIGNMENT;
+  if (stride_h < c->d && c->H > 1) return SIGATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < decode_ws_bytes(c)) return SIGATTN_ERR_INVALID_ARG;
+  const void* bufs[7] = {c->k, c->v, c->gate, c->count, c->seen, q, workspace};
+  for (int i = 0; i < 7; ++i) {
+    if (bufs[i] && bufs[i] == o) return SIGATTN_ERR_INVALID_ARG;
+    if (i < 6 && bufs[i] && bufs[i] == workspace) return SIGATTN_ERR_INVALID_ARG;
+  }
+  if (c->B == 0) return SIGATTN_OK;
+  sa::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.c = cache_view(c);
+  a.q = q;
+  a.out = o;
+  a.ws = static_cast<float*>(workspace);
+  a.qsb = stride_b;
+  a.qsh = stride_h;
+  a.B = c->B;
+  a.nchunk = (int32_t)decode_chunks(c);
+  a.out_f32 = out_dtype == SIGATTN_F32 ? 1 : 0;
+  const double sc = scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)c->d);
+  a.c1 = (float)(-sc * kLog2eD);
+  for (int b = 0; b < c->B; ++b) a.c2[b] = (float)(-(double)bias[b] * kLog2eD);
+  return sa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? SIGATTN_OK : SIGATTN_ERR_HIP;
 }
 
 int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int64_t cap,

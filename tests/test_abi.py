@@ -195,3 +195,96 @@ def test_gate_gradient_entry_rejects_before_launch(lib):
     # a bad problem is still reported first
     p.d = 96
     assert f(ctypes.byref(p), q, q, q, q, dk, dv, dgh, dg, None) == 2
+
+
+def _cache(**kw):
+    c = S.CacheDesc()
+    c.struct_size = ctypes.sizeof(S.CacheDesc)
+    c.B, c.H, c.d, c.cap = 2, 3, 64, 1000
+    c.stride_b, c.stride_h, c.stride_l = 3 * 1000 * 64, 1000 * 64, 64
+    c.k, c.v, c.gate = 1 << 20, 1 << 21, 1 << 22
+    c.count, c.seen = 1 << 23, (1 << 23) + 64
+    c.gate_eps, c.gate_tau, c.gate_sink = 1e-8, 0.05, 4
+    for key, val in kw.items():
+        setattr(c, key, val)
+    return c
+
+
+def test_decode_workspace_size(lib):
+    c = _cache()
+    # B * H * ceil(cap / 512) * d floats
+    assert lib.sigattn_decode_workspace_size(ctypes.byref(c)) == 2 * 3 * 2 * 64 * 4
+    c.cap = 1024
+    assert lib.sigattn_decode_workspace_size(ctypes.byref(c)) == 2 * 3 * 2 * 64 * 4
+    c.cap = 1025
+    assert lib.sigattn_decode_workspace_size(ctypes.byref(c)) == 2 * 3 * 3 * 64 * 4
+    c.struct_size += 4
+    assert lib.sigattn_decode_workspace_size(ctypes.byref(c)) == -1
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda c: setattr(c, "d", 96), 2),
+    (lambda c: setattr(c, "cap", 0), 1),
+    (lambda c: setattr(c, "B", 300), 2),
+    (lambda c: setattr(c, "k", None), 1),
+    (lambda c: setattr(c, "v", (1 << 21) + 8), 3),
+    (lambda c: setattr(c, "count", (1 << 23) + 2), 3),
+    (lambda c: setattr(c, "seen", 1 << 23), 1),        # count and seen alias
+    (lambda c: setattr(c, "stride_l", 60), 1),
+    (lambda c: setattr(c, "stride_l", 68), 3),
+    (lambda c: setattr(c, "gate_tau", -1.0), 1),
+    (lambda c: setattr(c, "gate_sink", -1), 1),
+])
+def test_cache_validation_before_launch(lib, mutate, code):
+    """Every cache entry point validates the cache description first and enqueues nothing
+    on error (fake device pointers)."""
+    c = _cache()
+    mutate(c)
+    vp = ctypes.c_void_p
+    bias = (ctypes.c_float * 2)(-1.0, -2.0)
+    assert lib.sigattn_decode(ctypes.byref(c), vp(1 << 24), 3 * 64, 64, bias, 0.0,
+                              vp(1 << 25), 0, vp(1 << 26), 1 << 20, None) == code
+    assert lib.sigattn_cache_append(ctypes.byref(c), vp(1 << 24), vp(1 << 25), 3 * 64, 64,
+                                    vp(1 << 26), None, None) == code
+
+
+def test_decode_argument_checks(lib):
+    c = _cache()
+    vp = ctypes.c_void_p
+    bias = (ctypes.c_float * 2)(-1.0, -2.0)
+    q, o, ws = vp(1 << 24), vp(1 << 25), vp(1 << 26)
+    args = lambda **kw: dict(dict(q=q, sb=3 * 64, sh=64, bias=bias, scale=0.0, o=o, dt=0,
+                                  ws=ws, wsb=1 << 20), **kw)
+
+    def call(a):
+        return lib.sigattn_decode(ctypes.byref(c), a["q"], a["sb"], a["sh"], a["bias"],
+                                  a["scale"], a["o"], a["dt"], a["ws"], a["wsb"], None)
+    assert call(args(bias=None)) == 1
+    assert call(args(bias=(ctypes.c_float * 2)(float("nan"), 0.0))) == 1
+    assert call(args(wsb=100)) == 1                  # workspace too small
+    assert call(args(o=q)) == 1                      # output aliases the query
+    assert call(args(ws=o)) == 1                     # workspace aliases the output
+    assert call(args(dt=3)) == 2
+    assert call(args(q=vp((1 << 24) + 4))) == 3
+    assert call(args(sh=63)) == 3
+    assert call(args(scale=-1.0)) == 1
+
+
+def test_cache_build_checks(lib):
+    c = _cache()
+    vp = ctypes.c_void_p
+    p, keep = S.make_problem(2, 3, 512, 64, [512, 100], gate_ptr=1 << 27)
+    k, v = vp(1 << 28), vp(1 << 29)
+    f = lib.sigattn_cache_build
+    p.H = 4                                           # shape mismatch with the cache
+    assert f(ctypes.byref(c), ctypes.byref(p), k, v, None) == 1
+    p.H = 3
+    c.cap = 300                                       # a prefill longer than the cache
+    assert f(ctypes.byref(c), ctypes.byref(p), k, v, None) == 1
+    c.cap = 1000
+    c.gate = None                                     # gated prefill, ungated cache
+    assert f(ctypes.byref(c), ctypes.byref(p), k, v, None) == 1
+    c.gate = 1 << 22
+    p.dtype = 1
+    p.out_dtype = 1
+    assert f(ctypes.byref(c), ctypes.byref(p), k, v, None) == 2

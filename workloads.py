@@ -22,7 +22,15 @@ causal_gated_512       bf16   16  12  64   512    causal, all valid; RMS-normali
                                                   gate g = logistic(z), z ~ N(2, var 2)
 causal_forced_drop_512 bf16   16  12  64   512    as above, plus g = 0.01 on a seeded 20%
                                                   of keys j >= 4 (exercises hard dropping)
+decode_gpt2_512        bf16   16  12  64   512    KV cache of a 512-token prefill, gates as in
+                                                  causal_forced_drop_512; one decode query
+decode_long            bf16   32  16  128  16384  KV cache of prefills n ~ U{8192..16384},
+                                                  gates as above; one decode query
+decode_long_64         bf16   32  12  64   16384  same lengths and gates, d = 64
 =====================  =====  ==  ==  ===  =====  ===========================================
+
+Decode workloads (``generate_decode``) draw, in order: lengths, the prefill K and V,
+the prefill gates, then one new token per sequence (its query, key, value and gate).
 
 Draw order with ``numpy.random.default_rng(seed)``: lengths, Q, K, V, dO, gate. Draws
 are float32 standard normals, scaled, then rounded to bf16 (round to nearest even) for
@@ -36,8 +44,8 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "get", "generate", "round_to_bf16", "valid_pairs",
-           "flops_forward", "flops_backward"]
+__all__ = ["Workload", "WORKLOADS", "get", "generate", "generate_decode", "round_to_bf16",
+           "valid_pairs", "flops_forward", "flops_backward"]
 
 
 @dataclass(frozen=True)
@@ -76,6 +84,15 @@ WORKLOADS = {
         Workload("causal_forced_drop_512", "bf16", 16, 12, 64, 512, ("fixed", [512] * 16),
                  seed=8, causal=True, rmsnorm_qk=True,
                  gate=("logistic_normal", 2.0, 2.0, 0.2, 0.01), tau=0.05, sink=4),
+        Workload("decode_gpt2_512", "bf16", 16, 12, 64, 512, ("fixed", [512] * 16), seed=9,
+                 causal=True, rmsnorm_qk=True, gate=("logistic_normal", 2.0, 2.0, 0.2, 0.01),
+                 tau=0.05, sink=4, extra={"cap": 1024}),
+        Workload("decode_long", "bf16", 32, 16, 128, 16384, ("uniform", 8192, 16384), seed=10,
+                 gate=("logistic_normal", 2.0, 2.0, 0.2, 0.01), tau=0.05, sink=4,
+                 extra={"cap": 16384}),
+        Workload("decode_long_64", "bf16", 32, 12, 64, 16384, ("uniform", 8192, 16384),
+                 seed=11, gate=("logistic_normal", 2.0, 2.0, 0.2, 0.01), tau=0.05, sink=4,
+                 extra={"cap": 16384}),
     ]
 }
 
@@ -162,6 +179,44 @@ def generate(w: Workload | str, poison: bool = False, with_do: bool = True) -> d
                seqlens=seqlens, gate=gate, causal=w.causal, tau=w.tau, sink=w.sink,
                workload=w)
     return out
+
+
+def _gates(w: Workload, rng, shape):
+    kind, mean, var = w.gate[0], w.gate[1], w.gate[2]
+    assert kind == "logistic_normal"
+    z = rng.standard_normal(shape) * math.sqrt(var) + mean
+    gate = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    if len(w.gate) > 3:
+        frac, val = w.gate[3], w.gate[4]
+        pick = rng.random(shape) < frac
+        if len(shape) == 2:
+            pick[:, : w.sink] = False
+        gate[pick] = np.float32(val)
+    return gate
+
+
+def generate_decode(w: Workload | str) -> dict:
+    """A KV-cache workload: a prefill (K, V [B, H, L, d], gates [B, L], lengths) and one
+    new token per sequence (q, k, v [B, H, d], gate [B]). Values as in ``generate``."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    rng = np.random.default_rng(w.seed)
+    seqlens = _lengths(w, rng)
+    shape = (w.B, w.H, w.L, w.d)
+    k = rng.standard_normal(shape, dtype=np.float32) * np.float32(w.qk_std)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    gate = None if w.gate is None else _gates(w, rng, (w.B, w.L))
+    q_new = rng.standard_normal((w.B, w.H, w.d), dtype=np.float32) * np.float32(w.qk_std)
+    k_new = rng.standard_normal((w.B, w.H, w.d), dtype=np.float32) * np.float32(w.qk_std)
+    v_new = rng.standard_normal((w.B, w.H, w.d), dtype=np.float32)
+    g_new = None if w.gate is None else _gates(w, rng, (w.B,))
+    if w.rmsnorm_qk:
+        for t in (k, q_new, k_new):
+            t /= np.sqrt(np.mean(t * t, axis=-1, keepdims=True) + np.float32(1e-6))
+    k, v, q_new, k_new, v_new = (round_to_bf16(t) for t in (k, v, q_new, k_new, v_new))
+    return dict(k=k, v=v, gate=gate, seqlens=seqlens, q=q_new, k_new=k_new, v_new=v_new,
+                g_new=g_new, tau=w.tau, sink=w.sink, cap=int(w.extra.get("cap", w.L)),
+                workload=w)
 
 
 def valid_pairs(seqlens, causal: bool) -> int:
