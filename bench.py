@@ -10,7 +10,11 @@ head bidirectional, n(n+1)/2 causal. Inputs are resident in HBM before timing st
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_8k_s1]
                     [--no-cpu-baseline]
 
-Prints one JSON line.
+Prints one JSON line. With a decode workload (--workload decode_long, decode_long_64,
+decode_gpt2_512) a step is one sigattn_decode of one query per (sequence, head) against a
+KV cache built by threshold eviction from a synthetic prefill, and the metric is the
+algorithmic HBM bandwidth of that decode (live cached K and V rows and their gates, the
+query and the output, per second) against the 8 TB/s of HBM3E.
 """
 
 import argparse
@@ -103,7 +107,99 @@ def cpu_baseline(data, w, min_seconds):
     }
 
 
+def cpu_baseline_decode(data, w, bias, min_seconds):
+    """The oracle's cache compaction + decode, timed per sequence until `min_seconds`
+    have passed, as algorithmic bytes per second (the GPU metric's unit)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    t_dec, nbytes, seqs = 0.0, 0, 0
+    for b in range(w.B):
+        sub = {key: data[key][b:b + 1] for key in ("k", "v", "gate", "q")}
+        st = oracle.cache_compact(sub["k"], sub["v"], data["seqlens"][b:b + 1], data["cap"],
+                                  gate=sub["gate"], tau=w.tau, sink=w.sink)
+        t0 = time.perf_counter()
+        oracle.decode(sub["q"], *st[:4], bias[b:b + 1])
+        t_dec += time.perf_counter() - t0
+        nbytes += decode_bytes(st[3], w.H, w.d, 4)
+        seqs += 1
+        if t_dec >= min_seconds:
+            break
+    return {"value": nbytes / t_dec / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle decode of {seqs} of the {w.B} sequences of {w.name} "
+                      f"(all heads), {t_dec:.2f} s; cache compaction untimed",
+            "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+
+
+def decode_bytes(counts, H, d, out_bytes):
+    """Algorithmic bytes of one decode: every live cached K and V row (bf16) and its gate
+    (float, read once per head), the bf16 query and the output of every (b, h)."""
+    live = int(np.sum(counts))
+    return live * H * (2 * d * 2 + 4) + len(counts) * H * d * (2 + out_bytes)
+
+
+def measure_decode(S, W, w, steps, warmup, no_cpu, cpu_seconds):
+    import math
+
+    import torch
+    data = W.generate_decode(w)
+    dev = torch.device("cuda:0")
+    B, H, L, d = data["k"].shape
+    cache = S.KVCache(B, H, d, data["cap"], gated=data["gate"] is not None, tau=w.tau,
+                      sink=w.sink)
+    cache.build(torch.from_numpy(data["k"]).to(torch.bfloat16).to(dev),
+                torch.from_numpy(data["v"]).to(torch.bfloat16).to(dev), data["seqlens"],
+                gate=None if data["gate"] is None else torch.from_numpy(data["gate"]).to(dev))
+    q = torch.from_numpy(data["q"]).to(torch.bfloat16).to(dev)
+    bias = np.array([-math.log(max(int(n), 1)) for n in data["seqlens"]])
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, cache.workspace_size() // 4), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        cache.decode(q, bias, out=out, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for e in evs:
+        e[0].record(stream)
+        cache.decode(q, bias, out=out, out_dtype=torch.float32, workspace=ws)
+        e[1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    ms_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    counts = cache.count.cpu().numpy()
+    nbytes = decode_bytes(counts, H, d, 4)
+    res = {
+        "metric": "decode HBM bandwidth, bf16 sigmoid attention against a KV cache with "
+                  "threshold eviction (GB/s of algorithmic bytes)",
+        "value": nbytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "d": d, "cap": data["cap"],
+                   "prefill_lengths": [int(x) for x in data["seqlens"]],
+                   "live_entries": [int(x) for x in counts], "tau": w.tau, "sink": w.sink,
+                   "step": "sigattn_decode (decode kernel + chunk reduction)"},
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel + decode_reduce_kernel",
+                     "achieved": nbytes / (ms_dec * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": nbytes / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": traffic_for(w.name, "decode")},
+        "algorithmic_bytes": nbytes,
+    }
+    if not no_cpu:
+        res["cpu_baseline"] = cpu_baseline_decode(data, w, bias, cpu_seconds)
+    return res
+
+
 PASS_KERNELS = {"fwd": "fwd_kernel", "bwd_dq": "dq_kernel", "bwd_dkdv": "dkdv_kernel"}
+DECODE_KERNELS = {"decode": "decode_kernel"}
 COPY_ELEMS = 64 << 20          # float32 elements read and written by the calibration copy
 
 
@@ -164,7 +260,8 @@ def pmc_collect(workload, fetch_csv, write_csv):
                    f"--workload {workload}; the same with WRITE_SIZE; then python bench.py "
                    f"--workload {workload} --pmc-collect <fetch csv> <write csv>",
     }
-    for name, key in PASS_KERNELS.items():
+    keys = DECODE_KERNELS if workload.startswith("decode") else PASS_KERNELS
+    for name, key in keys.items():
         fk, wk = pick(fetch, key), pick(write, key)
         hbm = fk * 1024.0 * out["calibration"]["fetch_factor"] + wk * 1024.0 * out["calibration"]["write_factor"]
         out["kernels"][name] = {"fetch_kib": fk, "write_kib": wk, "hbm_bytes": hbm}
@@ -185,6 +282,26 @@ def traffic_for(workload, kernel):
     if t.get("source_hash") != source_hash():
         return None
     return t["kernels"].get(kernel, {}).get("hbm_bytes")
+
+
+def pmc_pass_decode(S, W, w):
+    import math
+
+    import torch
+    data = W.generate_decode(w)
+    B, H, L, d = data["k"].shape
+    cache = S.KVCache(B, H, d, data["cap"], gated=True, tau=w.tau, sink=w.sink)
+    cache.build(torch.from_numpy(data["k"]).to(torch.bfloat16).cuda(),
+                torch.from_numpy(data["v"]).to(torch.bfloat16).cuda(), data["seqlens"],
+                gate=torch.from_numpy(data["gate"]).cuda())
+    q = torch.from_numpy(data["q"]).to(torch.bfloat16).cuda()
+    bias = [-math.log(max(int(n), 1)) for n in data["seqlens"]]
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 2.0, out=dst)
+    for _ in range(3):
+        cache.decode(q, bias, out_dtype=torch.float32)
+    torch.cuda.synchronize()
 
 
 def pmc_pass(S, w, t, gate, sl, out_dtype, fast_math):
@@ -223,6 +340,13 @@ def main():
         sys.exit(1)
     S.load()
     w = W.WORKLOADS[args.workload]
+    if w.name.startswith("decode"):
+        if args.pmc_pass:
+            pmc_pass_decode(S, W, w)
+            return
+        print(json.dumps(measure_decode(S, W, w, args.steps, args.warmup, args.no_cpu_baseline,
+                                        args.cpu_seconds)))
+        return
     data = W.generate(w)
     dev = torch.device("cuda:0")
     t = {k: torch.from_numpy(data[k]).to(torch.bfloat16).to(dev) for k in ("q", "k", "v", "do")}
