@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--pmc-collect", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the counter_collection.csv files of a FETCH_SIZE run and a "
                          "WRITE_SIZE run of --pmc-pass into profiles/traffic_<workload>.json")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the pages' kernel sweep: L = 512..16384 at B*L = 16384 tokens, d = 64 "
+                         "(32 heads) and 128 (16 heads), 0 %% and 25 %% padding; forward and "
+                         "backward TFLOPS, mean and 99 %% interval over 250 iterations")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="lower bound on the oracle time of the CPU baseline sample")
     return ap.parse_args()
@@ -339,6 +343,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     S.load()
+    if args.sweep:
+        print(json.dumps(sweep(S, W, iters=250, fast_math=args.fast_math)))
+        return
     w = W.WORKLOADS[args.workload]
     if w.name.startswith("decode"):
         if args.pmc_pass:
@@ -370,6 +377,67 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(data, w, args.cpu_seconds)
     print(json.dumps(res))
+
+
+def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False):
+    """The kernel sweep of the sigmoid-attention paper's section 4.1 ("Kernel
+    Performance"): sequence length 512..16384 with the batch set so that B * L = 16384
+    tokens, head dimension 64 (32 heads) and 128 (16 heads) of a 2048-wide model, 0 % and
+    25 % padding; bidirectional. Per configuration the forward and the backward
+    (dQ pass + dK/dV pass) are timed separately, each for `iters` iterations after about
+    `warmup_ms` of warm-up, with a pair of HIP events per iteration on the launch stream;
+    TFLOPS count valid tokens only."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for d, H in ((64, 32), (128, 16)):
+        for pad in (0.0, 0.25):
+            for L in (512, 1024, 2048, 4096, 8192, 16384):
+                B = 16384 // L
+                w = W.Workload(f"sweep_L{L}_d{d}_p{int(pad * 100)}", "bf16", B, H, d, L,
+                               ("mean_pad", pad), seed=1000 + L + d + int(pad * 100))
+                data = W.generate(w)
+                t = {k: torch.from_numpy(data[k]).to(torch.bfloat16).to(dev)
+                     for k in ("q", "k", "v", "do")}
+                sl = data["seqlens"]
+                kw = dict(out_dtype=torch.float32, fast_math=fast_math)
+                o = torch.empty(t["q"].shape, dtype=torch.float32, device=dev)
+                dq, dk, dv = torch.empty_like(o), torch.empty_like(o), torch.empty_like(o)
+
+                def fwd():
+                    S.fwd(t["q"], t["k"], t["v"], sl, out=o, **kw)
+
+                def bwd():
+                    S.bwd_dq(t["q"], t["k"], t["v"], t["do"], sl, out=dq, **kw)
+                    S.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], sl, out=(dk, dv), **kw)
+
+                res = {"L": L, "B": B, "H": H, "d": d, "padding": pad,
+                       "seqlens": [int(x) for x in sl]}
+                for name, fn, flops in (("fwd", fwd, W.flops_forward(sl, H, d, False)),
+                                        ("bwd", bwd, W.flops_backward(sl, H, d, False))):
+                    t0 = time.perf_counter()
+                    while time.perf_counter() - t0 < warmup_ms * 1e-3:
+                        fn()
+                        torch.cuda.synchronize()
+                    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                           for _ in range(iters)]
+                    for e0, e1 in evs:
+                        e0.record(stream)
+                        fn()
+                        e1.record(stream)
+                    torch.cuda.synchronize()
+                    ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+                    tf = flops / (ms * 1e-3) / 1e12
+                    half = 2.576 * float(np.std(tf, ddof=1)) / np.sqrt(len(tf))
+                    res[name] = {"ms": float(ms.mean()), "tflops": float(tf.mean()),
+                                 "ci99": half, "pct_peak": 100.0 * float(tf.mean()) / PEAK_BF16_TFLOPS}
+                rows.append(res)
+                print(f"[sweep] d={d} pad={pad} L={L} B={B}: fwd {res['fwd']['tflops']:.1f} "
+                      f"bwd {res['bwd']['tflops']:.1f} TFLOPS", file=sys.stderr, flush=True)
+    return {"sweep": "kernel sweep, B*L = 16384 tokens, bidirectional, bf16 inputs, float "
+                     "outputs, " + ("single bf16 operands" if fast_math else "hi+lo operands"),
+            "iters": iters, "rows": rows}
 
 
 def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):

@@ -102,7 +102,8 @@ def _sample_rows(n, L, rng, tile=64):
 
 
 @pytest.mark.parametrize("name", ["bidir_2k", "long_8k_s1", "long_8k_s4",
-                                  "pad_sweep_0", "pad_sweep_25", "pad_sweep_50"])
+                                  "pad_sweep_0", "pad_sweep_25", "pad_sweep_50",
+                                  "sweep_16k_d64_p25", "sweep_16k_d128", "sweep_512_d128_p25"])
 def test_full_size_sampled(name):
     """Full-size workloads in the launch configuration the benchmark times, checked on
     sampled rows that the oracle computes one by one."""

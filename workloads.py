@@ -22,6 +22,9 @@ causal_gated_512       bf16   16  12  64   512    causal, all valid; RMS-normali
                                                   gate g = logistic(z), z ~ N(2, var 2)
 causal_forced_drop_512 bf16   16  12  64   512    as above, plus g = 0.01 on a seeded 20%
                                                   of keys j >= 4 (exercises hard dropping)
+sweep_16k_d64_p25      bf16   1   32  64   16384  kernel-sweep extremes (B*L = 16384 tokens):
+sweep_16k_d128         bf16   1   16  128  16384  25 % / 0 % padding; the sweep itself
+sweep_512_d128_p25     bf16   32  16  128  512    (bench.py --sweep) covers every L and d
 decode_gpt2_512        bf16   16  12  64   512    KV cache of a 512-token prefill, gates as in
                                                   causal_forced_drop_512; one decode query
 decode_long            bf16   32  16  128  16384  KV cache of prefills n ~ U{8192..16384},
@@ -84,6 +87,10 @@ WORKLOADS = {
         Workload("causal_forced_drop_512", "bf16", 16, 12, 64, 512, ("fixed", [512] * 16),
                  seed=8, causal=True, rmsnorm_qk=True,
                  gate=("logistic_normal", 2.0, 2.0, 0.2, 0.01), tau=0.05, sink=4),
+        # extremes of the kernel sweep (B * L = 16384 tokens, hidden 2048)
+        Workload("sweep_16k_d64_p25", "bf16", 1, 32, 64, 16384, ("mean_pad", 0.25), seed=12),
+        Workload("sweep_16k_d128", "bf16", 1, 16, 128, 16384, ("mean_pad", 0.0), seed=13),
+        Workload("sweep_512_d128_p25", "bf16", 32, 16, 128, 512, ("mean_pad", 0.25), seed=14),
         Workload("decode_gpt2_512", "bf16", 16, 12, 64, 512, ("fixed", [512] * 16), seed=9,
                  causal=True, rmsnorm_qk=True, gate=("logistic_normal", 2.0, 2.0, 0.2, 0.01),
                  tau=0.05, sink=4, extra={"cap": 1024}),
