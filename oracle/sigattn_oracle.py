@@ -41,6 +41,12 @@ Readings taken where the pages are silent (each is also listed in the design not
   dg_j = sum_i dS_ij / (g_j + eps) + v_j . sum_i P_ij dO_i, per head; the gate is shared
   by the heads, so the gradient of the shared gate is the sum over heads. The hard drop
   is a step function of g: a dropped key gets derivative 0, like a padded key.
+* Packed batches with separate query and key lengths (not in the pages; needed to run a
+  query shard of a sequence on one GPU): sequence b owns query rows cu_q[b]..cu_q[b+1]-1
+  and key rows cu_k[b]..cu_k[b+1]-1; beta_b = -log(nk_b) unless given; the causal rule
+  is aligned at the bottom right, key j allowed for query i iff j <= i + nk_b - nq_b,
+  which for nq = nk is the rule above and for a shard of queries s..s+m-1 given keys
+  0..s+m-1 is the rule of the full sequence.
 * Decode with eviction ([KV-evict] gate paragraphs): after prefill the entries with
   g_j < tau (j >= sink) are physically removed; each entry written during decode is kept
   or removed by the same rule when it is written; kept entries keep their log-gate on
@@ -85,6 +91,8 @@ __all__ = [
     "gate_grad",
     "gate_grad_rows",
     "row_mass",
+    "forward_varlen",
+    "backward_varlen",
     "cache_compact",
     "cache_append",
     "decode",
@@ -430,6 +438,77 @@ def row_mass(q, k, seqlens, causal=False, gate=None, tau=0.0, sink=DEFAULT_SINK,
                 P = _P(q[b, h, rows], k[b, h, :n], rows, cols, s, beta, logg, keep, causal)
                 R[b, h, rows] = P.sum(axis=1)
     return R
+
+
+# ----------------------------------------------------------------------------------
+# packed batches with separate query and key lengths
+# ----------------------------------------------------------------------------------
+
+def _varlen_P(qb, kb, s, beta, logg, keep, causal, diag):
+    """P[i, j] for one head of one packed sequence: keys kept, and (causal) j <= i + diag."""
+    x = s * (qb @ kb.T) + beta + logg[None, :]
+    allowed = np.broadcast_to(keep[None, :], x.shape).copy()
+    if causal:
+        i = np.arange(qb.shape[0])[:, None]
+        j = np.arange(kb.shape[0])[None, :]
+        allowed &= j <= i + diag
+    P = np.zeros_like(x)
+    P[allowed] = logistic(x[allowed])
+    return P
+
+
+def _varlen_seq(cu_q, cu_k, b, gate, tau, sink, eps, bias):
+    q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+    nq, nk = q1 - q0, k1 - k0
+    beta = (sequence_bias(nk) if nk > 0 else 0.0) if bias is None else float(bias[b])
+    g = None if gate is None else np.asarray(gate, dtype=np.float64)[k0:k1]
+    keep = kept_keys(nk, nk, g, tau, sink)
+    logg = np.zeros(nk) if g is None else np.log(g + eps)
+    return q0, q1, k0, k1, nk - nq, beta, g, keep, logg
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, causal=False, gate=None, tau=0.0, sink=DEFAULT_SINK,
+                   eps=GATE_EPS, scale=None, bias=None):
+    """O for packed sequences: q [Tq, H, d], k and v [Tk, H, d]; gate [Tk] or None.
+    Rows outside the sequences are 0."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    H, d = q.shape[1], q.shape[2]
+    s = _params(d, scale)
+    O = np.zeros_like(q)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1, diag, beta, g, keep, logg = _varlen_seq(cu_q, cu_k, b, gate, tau, sink,
+                                                                eps, bias)
+        if q1 == q0:
+            continue
+        for h in range(H):
+            vp = v[k0:k1, h] if g is None else v[k0:k1, h] * g[:, None]
+            P = _varlen_P(q[q0:q1, h], k[k0:k1, h], s, beta, logg, keep, causal, diag)
+            O[q0:q1, h] = P @ vp
+    return O
+
+
+def backward_varlen(q, k, v, do, cu_q, cu_k, causal=False, gate=None, tau=0.0,
+                    sink=DEFAULT_SINK, eps=GATE_EPS, scale=None, bias=None):
+    """(dQ, dK, dV) of sum(dO * O) for packed sequences (same layout as forward_varlen)."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    H, d = q.shape[1], q.shape[2]
+    s = _params(d, scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1, diag, beta, g, keep, logg = _varlen_seq(cu_q, cu_k, b, gate, tau, sink,
+                                                                eps, bias)
+        if q1 == q0 or k1 == k0:
+            continue
+        for h in range(H):
+            kh = k[k0:k1, h]
+            vp = v[k0:k1, h] if g is None else v[k0:k1, h] * g[:, None]
+            P = _varlen_P(q[q0:q1, h], kh, s, beta, logg, keep, causal, diag)
+            dS = (do[q0:q1, h] @ vp.T) * P * (1.0 - P)
+            dq[q0:q1, h] = s * (dS @ kh)
+            dk[k0:k1, h] = s * (dS.T @ q[q0:q1, h])
+            dvp = P.T @ do[q0:q1, h]
+            dv[k0:k1, h] = dvp if g is None else dvp * g[:, None]
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------------

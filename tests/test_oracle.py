@@ -698,3 +698,117 @@ def test_decode_closed_form_q_zero():
         w = Gc[b, :m] * (Gc[b, :m] + eps) / (n + Gc[b, :m] + eps)
         np.testing.assert_allclose(out[b], np.einsum("j,hjc->hc", w, Vc[b, :, :m]), rtol=1e-12)
     assert np.all(O.decode(np.zeros((B, H, d)), Kc, Vc, Gc, np.array([0, 0]), [0.0, 0.0]) == 0)
+
+
+# ----------------------------------------------------------------------------------
+# packed batches with separate query and key lengths
+# ----------------------------------------------------------------------------------
+
+def _pack(x, lens):
+    """[B, H, L, d] padded -> [sum(lens), H, d] packed."""
+    return np.concatenate([x[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)], axis=0)
+
+
+@pytest.mark.parametrize("variant", ["bidir", "causal", "gated"])
+def test_varlen_equal_lengths_is_the_padded_definition(variant):
+    """With nq = nk the packed functions are the padded ones on the same rows."""
+    B, H, L, d = 3, 2, 17, 4
+    lens = [17, 5, 0]
+    q, k, v, do = (_rand((B, H, L, d), 140 + s) for s in range(4))
+    kw = {}
+    g = np.random.default_rng(145).uniform(0.0, 1.0, (B, L))
+    if variant == "causal":
+        kw["causal"] = True
+    if variant == "gated":
+        kw.update(gate=g, tau=0.3, sink=2, causal=True)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    o = O.forward(q, k, v, lens, **kw)
+    grads = O.backward(q, k, v, do, lens, **kw)
+    kwv = dict(kw)
+    if "gate" in kwv:
+        kwv["gate"] = np.concatenate([g[b, :n] for b, n in enumerate(lens)])
+    ov = O.forward_varlen(_pack(q, lens), _pack(k, lens), _pack(v, lens), cu, cu, **kwv)
+    gv = O.backward_varlen(_pack(q, lens), _pack(k, lens), _pack(v, lens), _pack(do, lens),
+                           cu, cu, **kwv)
+    np.testing.assert_allclose(ov, _pack(o, lens), rtol=1e-13, atol=1e-15)
+    for a, b_ in zip(gv, grads):
+        np.testing.assert_allclose(a, _pack(b_, lens), rtol=1e-12, atol=1e-14)
+
+
+def test_varlen_query_shards_reassemble_the_causal_sequence():
+    """A causal sequence of N tokens split into query shards: the shard of rows s..s+m-1,
+    given keys 0..s+m-1 and the sequence's bias, reproduces those rows of O and dQ, and
+    the shards' dK and dV add up to the full ones (their sums over query rows split)."""
+    N, H, d, m = 24, 2, 4, 8
+    rng = np.random.default_rng(150)
+    q, k, v, do = (rng.standard_normal((1, H, N, d)) for _ in range(4))
+    bias = [O.sequence_bias(N)]
+    o = O.forward(q, k, v, [N], causal=True, bias=bias)
+    dq, dk, dv = O.backward(q, k, v, do, [N], causal=True, bias=bias)
+    dk_sum, dv_sum = np.zeros((N, H, d)), np.zeros((N, H, d))
+    for s0 in range(0, N, m):
+        qs = q[0, :, s0:s0 + m].transpose(1, 0, 2)
+        dos = do[0, :, s0:s0 + m].transpose(1, 0, 2)
+        ks = k[0, :, :s0 + m].transpose(1, 0, 2)
+        vs = v[0, :, :s0 + m].transpose(1, 0, 2)
+        cu_q, cu_k = np.array([0, m]), np.array([0, s0 + m])
+        os_ = O.forward_varlen(qs, ks, vs, cu_q, cu_k, causal=True, bias=bias)
+        np.testing.assert_allclose(os_, o[0, :, s0:s0 + m].transpose(1, 0, 2), rtol=1e-12, atol=1e-15)
+        gq, gk, gv = O.backward_varlen(qs, ks, vs, dos, cu_q, cu_k, causal=True, bias=bias)
+        np.testing.assert_allclose(gq, dq[0, :, s0:s0 + m].transpose(1, 0, 2), rtol=1e-11, atol=1e-14)
+        dk_sum[:s0 + m] += gk
+        dv_sum[:s0 + m] += gv
+    np.testing.assert_allclose(dk_sum, dk[0].transpose(1, 0, 2), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dv_sum, dv[0].transpose(1, 0, 2), rtol=1e-11, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_finite_differences(causal):
+    """nq != nk (including a sequence with more queries than keys): central differences
+    of <dO, O> match the packed backward."""
+    H, d = 1, 3
+    cu_q, cu_k = np.array([0, 3, 8]), np.array([0, 5, 7])
+    rng = np.random.default_rng(160)
+    q, do = rng.standard_normal((8, H, d)), rng.standard_normal((8, H, d))
+    k, v = rng.standard_normal((7, H, d)), rng.standard_normal((7, H, d))
+    g = rng.uniform(0.2, 1.0, 7)
+    kw = dict(causal=causal, gate=g)
+    grads = O.backward_varlen(q, k, v, do, cu_q, cu_k, **kw)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(do * O.forward_varlen(qq, kk, vv, cu_q, cu_k, **kw)))
+
+    h = 1e-6
+    for idx_t, (x, gx) in enumerate(zip((q, k, v), grads)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p, args_m = [q, k, v], [q, k, v]
+            args_p[idx_t], args_m[idx_t] = xp, xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(gx, num, rtol=1e-6, atol=1e-8)
+    if causal:
+        # sequence 1 has 5 queries and 2 keys: its first 3 queries see no key
+        o = O.forward_varlen(q, k, v, cu_q, cu_k, **kw)
+        assert np.all(o[3:6] == 0.0) and np.any(o[6:8] != 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_closed_form_qk_zero(causal):
+    """Q = K = 0 with nq != nk: every allowed weight is sigma(-ln nk) = 1/(nk + 1), so
+    O_i = sum over allowed keys of v_j / (nk + 1), the allowed keys being all nk of them,
+    or (causal, bottom right) j <= i + nk - nq."""
+    H, d = 2, 3
+    cu_q, cu_k = np.array([0, 4, 4, 10]), np.array([0, 9, 12, 14])
+    rng = np.random.default_rng(170)
+    q, k = np.zeros((10, H, d)), np.zeros((14, H, d))
+    v = rng.standard_normal((14, H, d))
+    o = O.forward_varlen(q, k, v, cu_q, cu_k, causal=causal)
+    for b in range(3):
+        nq, nk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for i in range(nq):
+            hi = min(nk, i + nk - nq + 1) if causal else nk
+            want = v[cu_k[b]:cu_k[b] + max(hi, 0)].sum(axis=0) / (nk + 1)
+            np.testing.assert_allclose(o[cu_q[b] + i], want, rtol=1e-13, atol=1e-15)
