@@ -144,6 +144,56 @@ sigattn_status sigattn_bwd_dkdv_dg(const sigattn_problem* p, const void* q, cons
                                    const void* v, const void* dout, void* dk, void* dv,
                                    float* dg_head, float* dg, void* stream);
 
+/* ------------------------- packed variable-length batches ---------------------------
+ *
+ * Sequences packed back to back without padding, their bounds in DEVICE arrays (so that a
+ * data loader or a previous kernel can produce them without a host round trip), query
+ * and key lengths that may differ, and no cap on B. Sequence b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q, o, dO, dq and key rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k, v, dk, dv; nq_b and nk_b are the
+ * differences. Every packed tensor is [rows][H][d] with element (t, h, c) at
+ * t * stride_t + h * stride_h + c. The operation per (b, h) is that of the padded entry
+ * points with n replaced by nq_b for queries and nk_b for keys; the bias defaults to
+ * beta_b = -ln(nk_b). Causal alignment is bottom right: key j is allowed for query i iff
+ * j <= i + nk_b - nq_b, so a query shard of rows s .. s+m-1 of a causal sequence, given
+ * the keys 0 .. s+m-1 and the sequence's bias, yields exactly those rows of the full
+ * result: the per-GPU share of context parallelism (outputs of key shards add up,
+ * there is no row maximum to merge). All query rows of every sequence are written (rows
+ * with no allowed key get 0), and all key rows of dk and dv; rows outside
+ * cu[0] .. cu[B]-1 are not touched. Only bf16 inputs; the row-mass and gate-gradient
+ * side outputs are not offered here.
+ */
+typedef struct sigattn_varlen {
+  uint32_t struct_size;          /* sizeof(sigattn_varlen): ABI check */
+  int32_t B, H, d;               /* B >= 0, H >= 1, d in {64,128} */
+  int32_t max_seqlen_q;          /* HOST bound: every nq_b <= max_seqlen_q (sizes the grid) */
+  int32_t max_seqlen_k;          /* HOST bound: every nk_b <= max_seqlen_k */
+  int32_t out_dtype;             /* sigattn_dtype of o, dq, dk, dv */
+  int32_t fast_math;             /* as in sigattn_problem */
+  int64_t stride_t, stride_h;    /* element strides of rows and heads, shared by all tensors */
+  const int32_t* cu_seqlens_q;   /* DEVICE int32 [B + 1], non-decreasing */
+  const int32_t* cu_seqlens_k;   /* DEVICE int32 [B + 1], non-decreasing */
+  int32_t causal;                /* 0 or 1 (bottom-right aligned) */
+  float scale;                   /* s; 0 selects 1/sqrt(d) */
+  const float* bias;             /* DEVICE float [B] or NULL (beta_b = -ln(nk_b)) */
+  const float* gate;             /* DEVICE float per packed key row (gate[cu_k[b] + j]) or NULL */
+  float gate_eps;
+  float gate_tau;
+  int32_t gate_sink;
+} sigattn_varlen;
+
+/* The bounds in cu_seqlens_q/k are read by the kernels and are not checked on the host;
+ * a sequence longer than max_seqlen_q (queries) or max_seqlen_k (keys) is computed only
+ * up to that bound. Returns SIGATTN_ERR_UNSUPPORTED when B * H * ceil(max / 128)
+ * exceeds 2^31 - 1 work items. */
+sigattn_status sigattn_fwd_varlen(const sigattn_varlen* p, const void* q, const void* k,
+                                  const void* v, void* o, void* stream);
+sigattn_status sigattn_bwd_dq_varlen(const sigattn_varlen* p, const void* q, const void* k,
+                                     const void* v, const void* dout, void* dq, void* stream);
+sigattn_status sigattn_bwd_dkdv_varlen(const sigattn_varlen* p, const void* q,
+                                       const void* k, const void* v, const void* dout,
+                                       void* dk, void* dv, void* stream);
+
 /* ------------------- KV cache with threshold eviction, single-query decode -------------------
  *
  * "Sigmoid Attention as a Better Substrate for Learned KV Cache Eviction", gate paragraphs:

@@ -11,6 +11,7 @@ raises, there is no fallback.
     dq = bwd_dq(q, k, v, do, seqlens, ...)
     dk, dv = bwd_dkdv(q, k, v, do, seqlens, ...)
     dk, dv, dg_head, dg = bwd_dkdv_dg(q, k, v, do, seqlens, gate=g, ...)
+    o = fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k)      # packed [rows, H, d] batches
     cache = KVCache(B, H, d, cap, gated=True, tau=0.05)   # KV cache with eviction
     cache.build(k, v, seqlens, gate=g); cache.append(k1, v1, g1); o1 = cache.decode(q1, bias)
 
@@ -27,7 +28,8 @@ import os
 
 import numpy as np
 
-__all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd_dkdv_dg", "KVCache", "CacheDesc",
+__all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd_dkdv_dg", "fwd_varlen",
+           "bwd_dq_varlen", "bwd_dkdv_varlen", "VarlenDesc", "KVCache", "CacheDesc",
            "validate", "plan", "library_path", "load",
            "Problem", "SigattnError", "STATUS", "VERSION"]
 
@@ -65,6 +67,22 @@ class Problem(ctypes.Structure):
         ("gate_stride_b", ctypes.c_int64),
         ("gate_eps", ctypes.c_float),
         ("gate_tau", ctypes.c_float),
+        ("gate_sink", ctypes.c_int32),
+    ]
+
+
+class VarlenDesc(ctypes.Structure):
+    """Mirror of ``sigattn_varlen`` in include/sigattn.h."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("fast_math", ctypes.c_int32),
+        ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("bias", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+        ("gate_eps", ctypes.c_float), ("gate_tau", ctypes.c_float),
         ("gate_sink", ctypes.c_int32),
     ]
 
@@ -107,6 +125,12 @@ def load():
     lib.sigattn_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dkdv_dg.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    VD = ctypes.POINTER(VarlenDesc)
+    lib.sigattn_fwd_varlen.argtypes = [VD, vp, vp, vp, vp, vp]
+    lib.sigattn_bwd_dq_varlen.argtypes = [VD, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_bwd_dkdv_varlen.argtypes = [VD, vp, vp, vp, vp, vp, vp, vp]
+    for f in (lib.sigattn_fwd_varlen, lib.sigattn_bwd_dq_varlen, lib.sigattn_bwd_dkdv_varlen):
+        f.restype = ctypes.c_int
     C = ctypes.POINTER(CacheDesc)
     i64 = ctypes.c_int64
     lib.sigattn_cache_build.argtypes = [C, P, vp, vp, vp]
@@ -448,3 +472,84 @@ class KVCache:
                                   workspace.numel() * 4, _stream(q))
         _check(code, "sigattn_decode")
         return out
+
+
+def _varlen_desc(q, k, tensors, cu_q, cu_k, max_q, max_k, causal, gate, tau, sink, eps,
+                 scale, bias, out_dtype, fast_math):
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or q.shape[1:] != k.shape[1:]:
+        raise ValueError("expected packed [rows, H, d] tensors with the same H and d")
+    for t in (q, k) + tuple(tensors):
+        if t.stride() != q.stride() or t.dtype != torch.bfloat16 or t.device != q.device:
+            raise ValueError("packed tensors must be bf16, on one GPU, with the same strides")
+    if q.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    for c in (cu_q, cu_k):
+        if c.dtype != torch.int32 or c.device != q.device or c.dim() != 1 or not c.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32 tensors on q's GPU")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need B + 1 entries each")
+    for x in (gate, bias):
+        if x is not None and (x.dtype != torch.float32 or x.device != q.device or not x.is_contiguous()):
+            raise ValueError("gate and bias must be contiguous float32 tensors on q's GPU")
+    p = VarlenDesc()
+    p.struct_size = ctypes.sizeof(VarlenDesc)
+    p.B, p.H, p.d = cu_q.numel() - 1, q.shape[1], q.shape[2]
+    p.max_seqlen_q, p.max_seqlen_k = int(max_q), int(max_k)
+    p.out_dtype = F32 if out_dtype == torch.float32 else BF16
+    p.fast_math = 1 if fast_math else 0
+    p.stride_t, p.stride_h = q.stride(0), q.stride(1)
+    p.cu_seqlens_q, p.cu_seqlens_k = cu_q.data_ptr(), cu_k.data_ptr()
+    p.causal = 1 if causal else 0
+    p.scale = float(scale)
+    p.bias = None if bias is None else bias.data_ptr()
+    p.gate = None if gate is None else gate.data_ptr()
+    p.gate_eps, p.gate_tau, p.gate_sink = float(eps), float(tau), int(sink)
+    return p
+
+
+def _new_like(x, out_dtype):
+    torch = _torch()
+    dt = torch.bfloat16 if out_dtype is None else out_dtype
+    return torch.empty_strided(x.shape, x.stride(), dtype=dt, device=x.device)
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, *, causal=False, gate=None, tau=0.0,
+               sink=4, eps=1e-8, scale=0.0, bias=None, out=None, out_dtype=None,
+               fast_math=False):
+    """O for packed sequences: q [rows_q, H, d], k, v [rows_k, H, d] (bf16); cu_q, cu_k
+    device int32 [B + 1]; max_q, max_k host bounds on the sequence lengths; gate device
+    float per key row; bias device float [B] (default -ln(nk))."""
+    lib = load()
+    p = _varlen_desc(q, k, (v,), cu_q, cu_k, max_q, max_k, causal, gate, tau, sink, eps, scale,
+                     bias, out_dtype, fast_math)
+    out = _new_like(q, out_dtype) if out is None else out
+    _check(lib.sigattn_fwd_varlen(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  out.data_ptr(), _stream(q)), "sigattn_fwd_varlen")
+    return out
+
+
+def bwd_dq_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k, *, causal=False, gate=None, tau=0.0,
+                  sink=4, eps=1e-8, scale=0.0, bias=None, out=None, out_dtype=None,
+                  fast_math=False):
+    lib = load()
+    p = _varlen_desc(q, k, (v, do), cu_q, cu_k, max_q, max_k, causal, gate, tau, sink, eps,
+                     scale, bias, out_dtype, fast_math)
+    out = _new_like(q, out_dtype) if out is None else out
+    _check(lib.sigattn_bwd_dq_varlen(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     do.data_ptr(), out.data_ptr(), _stream(q)),
+           "sigattn_bwd_dq_varlen")
+    return out
+
+
+def bwd_dkdv_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k, *, causal=False, gate=None,
+                    tau=0.0, sink=4, eps=1e-8, scale=0.0, bias=None, out=None, out_dtype=None,
+                    fast_math=False):
+    lib = load()
+    p = _varlen_desc(q, k, (v, do), cu_q, cu_k, max_q, max_k, causal, gate, tau, sink, eps,
+                     scale, bias, out_dtype, fast_math)
+    dk, dv = (_new_like(k, out_dtype), _new_like(k, out_dtype)) if out is None else out
+    _check(lib.sigattn_bwd_dkdv_varlen(ctypes.byref(p), q.data_ptr(), k.data_ptr(),
+                                       v.data_ptr(), do.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                       _stream(q)), "sigattn_bwd_dkdv_varlen")
+    return dk, dv

@@ -45,7 +45,7 @@ __device__ __forceinline__ constexpr int kv_arc(int r) { return 8 * (r >> 2) + (
 
 // K, V, dK and dV of 32 keys take 96 registers per lane at d = 64 (two waves per SIMD)
 // and 192 at d = 128 (one wave per SIMD).
-template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool DG>
+template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool DG, bool VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
 void dkdv_kernel(const KArgs a) {
   using T = DkvTraits<D, CPT>;
@@ -56,14 +56,16 @@ void dkdv_kernel(const KArgs a) {
   const int l = lane_id(), w = wave_id();
   const int lk = 4 * (l >> 5);
   const SplitSel sel;
-  const Item it = block_item(a);
-  const int n = it.n;
-  const int last = n - 1;
-  const int64_t hoff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
-  const bf16* Qg = (const bf16*)a.q + hoff;
-  const bf16* Kg = (const bf16*)a.k + hoff;
-  const bf16* Vg = (const bf16*)a.v + hoff;
-  const bf16* dOg = (const bf16*)a.dout + hoff;
+  // VL: packed batch (separate query and key lengths, bottom-right causal diagonal)
+  const Item it = block_item<VL>(a);
+  if (VL && !it.valid) return;
+  const int nq = it.nq, nk = VL ? it.nk : it.nq, diag = VL ? it.diag : 0;
+  const int lastq = nq - 1, lastk = nk - 1;
+  const int64_t koff = VL ? it.koff : it.qoff;
+  const bf16* Qg = (const bf16*)a.q + it.qoff;
+  const bf16* Kg = (const bf16*)a.k + koff;
+  const bf16* Vg = (const bf16*)a.v + koff;
+  const bf16* dOg = (const bf16*)a.dout + it.qoff;
   const int64_t sl = a.sl;
   const int item_k0 = it.t * T::BK;
   const int k0 = item_k0 + w * 32;          // first key of this wave
@@ -73,26 +75,30 @@ void dkdv_kernel(const KArgs a) {
   // per-lane key constants: logit offset (exp2 domain; +inf drops the key) and factor
   float c2 = it.c2, gmul = 1.0f, gval = 1.0f;
   if (GATED) {
-    gval = a.gate[(int64_t)it.b * a.gsb + (mykey < last ? mykey : last)];
-    const bool keep = mykey < n && !(mykey >= a.gate_sink && gval < a.gate_tau);
+    gval = a.gate[it.goff + (mykey < lastk ? mykey : lastk)];
+    const bool keep = mykey < nk && !(mykey >= a.gate_sink && gval < a.gate_tau);
     c2 = keep ? c2 - __builtin_amdgcn_logf(gval + a.gate_eps) : __builtin_inff();
     gmul = keep ? gval : 0.0f;
   }
   float ds_sum = 0.0f;   // DG: sum over this lane's queries of dS / g_j
 
-  // query chunks of the item: all valid queries, or (causal) those from the item's
-  // first key on; this wave's first contributing chunk is c_lo
-  const int nch = (n + 31) / 32;
-  const int c_start = CAUSAL ? item_k0 / 32 : 0;
+  // query chunks of the item: all valid queries, or (causal) those from the first query
+  // allowed for the item's first key (key j is seen by queries i >= j - diag); this
+  // wave's first contributing chunk is c_lo
+  const int nch = (nq + 31) / 32;
+  const int c_start = CAUSAL ? (item_k0 - diag > 0 ? item_k0 - diag : 0) / 32 : 0;
   const int t0 = c_start / CPT;
   const int ntiles = (nch + CPT - 1) / CPT;
-  int c_lo = CAUSAL ? k0 / 32 : 0;
-  if (k0 >= n) c_lo = nch;                  // all keys of this wave are padding
+  int c_lo = CAUSAL ? (k0 - diag > 0 ? k0 - diag : 0) / 32 : 0;
+  if (k0 >= nk) c_lo = nch;                 // all keys of this wave are padding
+  // S of the first unit is formed before the tile loop when its tile is one of the two
+  // loaded first, else at the start of that unit (a causal shift can put it later)
+  const bool s_late = VL && CAUSAL && PIPE && c_lo < nch && c_lo / CPT > t0 + 1;
 
   auto issue_tile = [&](int t) {
     char* st = smem + (t % T::NSTAGE) * T::STAGE;
-    Tile::load(st, Qg, sl, t * T::BQ, last);
-    Tile::load(st + T::TILE, dOg, sl, t * T::BQ, last);
+    Tile::load(st, Qg, sl, t * T::BQ, lastq);
+    Tile::load(st + T::TILE, dOg, sl, t * T::BQ, lastq);
   };
   if (t0 < ntiles) issue_tile(t0);
   if (t0 + 1 < ntiles) issue_tile(t0 + 1);
@@ -100,7 +106,7 @@ void dkdv_kernel(const KArgs a) {
   // K and V rows as B operands: lane holds key mykey, d = 16ks + 8(l/32) + 0..7
   bf16x8 kreg[T::KS], vreg[T::KS];
   {
-    const int row = mykey < last ? mykey : last;
+    const int row = mykey < lastk ? mykey : lastk;
     const bf16* kr = Kg + (int64_t)row * sl + 8 * (l >> 5);
     const bf16* vr = Vg + (int64_t)row * sl + 8 * (l >> 5);
 #pragma unroll
@@ -123,19 +129,19 @@ void dkdv_kernel(const KArgs a) {
 
   // S of this wave's first chunk (its tile is one of the two loaded above)
   f32x16 s_cur = zero16();
-  if (PIPE && c_lo < nch) {
+  if (PIPE && c_lo < nch && !s_late) {
     const char* st = smem + ((c_lo / CPT) % T::NSTAGE) * T::STAGE;
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks)
       s_cur = mfma(lds_row_operand<D>(st, (c_lo % CPT) * 32, 16 * ks), kreg[ks], s_cur);
   }
 
-  // logistic of the 16 entries of S(c), masked (query < n; key <= query if causal)
+  // logistic of the 16 entries of S(c), masked (query < nq; query >= key - diag if causal)
   auto sig16 = [&](auto mode_tag, int qb0, f32x16& p) {
     constexpr int MODE = decltype(mode_tag)::value;
-    // keep query >= lo_q and query <= last: query = qb0 + lk + arc(r)
-    const int hi_lim = last - qb0 - lk;
-    const int lo_lim = mykey - qb0 - lk;
+    // keep query >= mykey - diag and query <= lastq: query = qb0 + lk + arc(r)
+    const int hi_lim = lastq - qb0 - lk;
+    const int lo_lim = mykey - diag - qb0 - lk;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float x = sigmoid_l2(s_cur[r], c1, c2);
@@ -258,10 +264,12 @@ void dkdv_kernel(const KArgs a) {
   };
 
   // Tile loops: [t0, tm1) masked (the causal diagonal chunk), [tm1, tm2) interior,
-  // [tm2, ntiles) masked (the chunk holding the last valid query when n % 32 != 0).
+  // [tm2, ntiles) masked (the chunk holding the last valid query when nq % 32 != 0).
   // Every wave passes one barrier per tile.
-  int tm1 = CAUSAL ? c_lo / CPT + 1 : t0;
-  int tm2 = (n % 32 != 0) ? (nch - 1) / CPT : ntiles;
+  // masked under the causal rule: chunks up to the one holding query k0 + 31 - diag
+  int tm1 = t0;
+  if (CAUSAL && k0 + 31 - diag >= 0) tm1 = (k0 + 31 - diag) / 32 / CPT + 1;
+  int tm2 = (nq % 32 != 0) ? (nch - 1) / CPT : ntiles;
   if (c_lo >= nch) { tm1 = ntiles; tm2 = ntiles; }
   tm1 = tm1 < ntiles ? tm1 : ntiles;
   tm2 = tm2 > tm1 ? tm2 : tm1;
@@ -278,6 +286,12 @@ void dkdv_kernel(const KArgs a) {
       const int c = t * CPT + cc;
       if (MODE == kKvInterior || (c >= c_lo && c < nch)) {
         if (PIPE) {
+          if (MODE == kKvMasked && s_late && c == c_lo) {
+            s_cur = zero16();
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks)
+              s_cur = mfma(lds_row_operand<D>(cur, cc * 32, 16 * ks), kreg[ks], s_cur);
+          }
           const char* Qn = (cc + 1 < CPT) ? cur : nxt;
           unit(mode_tag, cur, cur + T::TILE, cc * 32, Qn, ((cc + 1) % CPT) * 32, c * 32);
         } else {
@@ -294,7 +308,7 @@ void dkdv_kernel(const KArgs a) {
     // v_j . (sum_i P_ij dO_i): this lane holds features 32 dt + 8 m + lk + e of the dV
     // accumulator (before the gate factor); the partner lane (l ^ 32) holds the rest
     float vdot = 0.0f;
-    if (mykey < n) {
+    if (mykey < nk) {
       const bf16* vr = Vg + (int64_t)mykey * sl + lk;
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
@@ -307,15 +321,15 @@ void dkdv_kernel(const KArgs a) {
     }
     ds_sum += __shfl_xor(ds_sum, 32, 64);
     vdot += __shfl_xor(vdot, 32, 64);
-    if (l < 32 && mykey < n) {
+    if (l < 32 && mykey < nk) {
       // dS = g_j * ds_sum terms (the kernel's dP omits the gate factor of V'_j)
       const float dg = gmul != 0.0f ? gval / (gval + a.gate_eps) * ds_sum + vdot : 0.0f;
       a.aux[((int64_t)it.b * a.H + it.h) * a.Lmax + mykey] = dg;
     }
   }
 
-  if (mykey < n) {
-    const int64_t roff = hoff + (int64_t)mykey * sl;
+  if (mykey < nk) {
+    const int64_t roff = koff + (int64_t)mykey * sl;
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) {
       store_row(a.out0, roff, a.out_f32, dk[dt], 32 * dt, a.scale * gmul);
@@ -326,7 +340,10 @@ void dkdv_kernel(const KArgs a) {
 
 template <int D, int CPT, bool C, bool G, bool SP, bool DG = false>
 static hipError_t launch_one(const KArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((dkdv_kernel<D, CPT, C, G, SP, DG>), dim3(a.nitems), dim3(256), 0, st, a);
+  if (a.varlen)
+    hipLaunchKernelGGL((dkdv_kernel<D, CPT, C, G, SP, false, true>), dim3(a.nitems), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<D, CPT, C, G, SP, DG, false>), dim3(a.nitems), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ enum DqMode { kDqInterior = 0, kDqMasked = 1 };
 
 __device__ __forceinline__ constexpr int dq_arc(int r) { return 8 * (r >> 2) + (r & 3); }
 
-template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT>
+template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(const KArgs a) {
   using T = DqTraits<D, CPT, GATED>;
@@ -46,53 +46,60 @@ void dq_kernel(const KArgs a) {
   const int l = lane_id(), w = wave_id();
   const int lk = 4 * (l >> 5);
   const SplitSel sel;
-  const Item it = block_item(a);
-  const int n = it.n;
-  const int last = n - 1;
-  const int64_t hoff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
-  const bf16* Qg = (const bf16*)a.q + hoff;
-  const bf16* Kg = (const bf16*)a.k + hoff;
-  const bf16* Vg = (const bf16*)a.v + hoff;
-  const bf16* dOg = (const bf16*)a.dout + hoff;
-  const float* Gg = GATED ? a.gate + (int64_t)it.b * a.gsb : nullptr;
+  // VL: packed batch (separate query and key lengths, bottom-right causal diagonal)
+  const Item it = block_item<VL>(a);
+  if (VL && !it.valid) return;
+  const int nq = it.nq, nk = VL ? it.nk : it.nq, diag = VL ? it.diag : 0;
+  const int lastq = nq - 1, lastk = nk - 1;
+  const int64_t koff = VL ? it.koff : it.qoff;
+  const bf16* Qg = (const bf16*)a.q + it.qoff;
+  const bf16* Kg = (const bf16*)a.k + koff;
+  const bf16* Vg = (const bf16*)a.v + koff;
+  const bf16* dOg = (const bf16*)a.dout + it.qoff;
+  const float* Gg = GATED ? a.gate + it.goff : nullptr;
   const int64_t sl = a.sl;
   const int item_q0 = it.t * T::BM;
   const int q0 = item_q0 + w * 32;
   const float c1 = a.c1, c2 = it.c2;
 
-  int kend = n;
-  if (CAUSAL) kend = (item_q0 + T::BM < n) ? item_q0 + T::BM : n;
+  int kend = nk;
+  if (CAUSAL) {
+    const int e = (item_q0 + T::BM < nq ? item_q0 + T::BM : nq) + diag;
+    kend = e < 0 ? 0 : (e < nk ? e : nk);
+  }
   const int nch = (kend + 31) / 32;
   const int ntiles = (nch + CPT - 1) / CPT;
-  int wch = q0 < n ? nch : 0;
-  if (CAUSAL && q0 < n) {
-    const int lastq = (q0 + 32 < n ? q0 + 32 : n) - 1;
-    wch = lastq / 32 + 1 < nch ? lastq / 32 + 1 : nch;
+  int wch = q0 < nq ? nch : 0;
+  if (CAUSAL && q0 < nq) {
+    const int lk_allowed = (q0 + 32 < nq ? q0 + 32 : nq) - 1 + diag;
+    wch = lk_allowed < 0 ? 0 : (lk_allowed / 32 + 1 < nch ? lk_allowed / 32 + 1 : nch);
   }
 
   auto issue_tile = [&](int t) {
     char* st = smem + (t % T::NSTAGE) * T::STAGE;
-    Tile::load(st, Kg, sl, t * T::BN, last);
-    Tile::load(st + T::TILE, Vg, sl, t * T::BN, last);
+    Tile::load(st, Kg, sl, t * T::BN, lastk);
+    Tile::load(st + T::TILE, Vg, sl, t * T::BN, lastk);
   };
   auto fill_table = [&](int t) {
     if (GATED && w == 0 && l < T::BN) {
       float* tab = reinterpret_cast<float*>(smem + (t % T::NSTAGE) * T::STAGE + 2 * T::TILE);
       const int key = t * T::BN + l;
-      const float g = Gg[key < last ? key : last];
-      const bool keep = key < n && !(key >= a.gate_sink && g < a.gate_tau);
+      const float g = Gg[key < lastk ? key : lastk];
+      const bool keep = key < nk && !(key >= a.gate_sink && g < a.gate_tau);
       tab[l] = keep ? c2 - __builtin_amdgcn_logf(g + a.gate_eps) : __builtin_inff();
       tab[T::BN + l] = keep ? g : 0.0f;
     }
   };
-  issue_tile(0);
+  if (ntiles > 0) {
+    issue_tile(0);
+    fill_table(0);
+  }
   if (ntiles > 1) issue_tile(1);
-  fill_table(0);
 
   bf16x8 qop[T::KS], doop[T::KS];
   {
     int row = q0 + (l & 31);
-    row = row < last ? row : last;
+    row = row < lastq ? row : lastq;
     const bf16* qr = Qg + (int64_t)row * sl + 8 * (l >> 5);
     const bf16* dr = dOg + (int64_t)row * sl + 8 * (l >> 5);
 #pragma unroll
@@ -129,9 +136,9 @@ void dq_kernel(const KArgs a) {
       tc2 = *reinterpret_cast<const f32x4*>(tab + krow + 2 * r0 + lk);
       tg = *reinterpret_cast<const f32x4*>(tab + T::BN + krow + 2 * r0 + lk);
     }
-    int lim = n - 1 - kb - lk;
+    int lim = nk - 1 - kb - lk;
     if (CAUSAL) {
-      const int ld = q0 + (l & 31) - kb - lk;
+      const int ld = q0 + (l & 31) + diag - kb - lk;
       lim = ld < lim ? ld : lim;
     }
 #pragma unroll
@@ -233,11 +240,14 @@ void dq_kernel(const KArgs a) {
   };
   constexpr bool PIPE = D == 64;
 
-  int cfirst = n / 32;
-  if (CAUSAL) cfirst = (q0 + 1) / 32 < cfirst ? (q0 + 1) / 32 : cfirst;
+  int cfirst = nk / 32;
+  if (CAUSAL) {
+    const int c = q0 + diag + 1 < 0 ? 0 : (q0 + diag + 1) / 32;
+    cfirst = c < cfirst ? c : cfirst;
+  }
   int tmask = cfirst / CPT;
   tmask = tmask < ntiles ? tmask : ntiles;
-  if (q0 >= n) tmask = 0;
+  if (q0 >= nq) tmask = 0;
 
   // `stage`: the ring slot of tile t, a compile-time constant in the unrolled interior
   // loop (LDS addresses fold into immediate offsets), or -1 when computed
@@ -279,16 +289,19 @@ void dq_kernel(const KArgs a) {
   for (int dt = 0; dt < T::DT; ++dt) dq_mfma(dt, dkc[dt], dsh, dsl);
 
   const int query = q0 + (l & 31);
-  if (query < n) {
+  if (query < nq) {
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt)
-      store_row(a.out0, hoff + (int64_t)query * sl, a.out_f32, acc[dt], 32 * dt, a.scale);
+      store_row(a.out0, it.qoff + (int64_t)query * sl, a.out_f32, acc[dt], 32 * dt, a.scale);
   }
 }
 
 template <int D, int CPT, bool C, bool G, bool SP>
 static hipError_t launch_one(const KArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((dq_kernel<D, CPT, C, G, SP>), dim3(a.nitems), dim3(256), 0, st, a);
+  if (a.varlen)
+    hipLaunchKernelGGL((dq_kernel<D, CPT, C, G, SP, true>), dim3(a.nitems), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, CPT, C, G, SP, false>), dim3(a.nitems), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -242,13 +242,51 @@ struct DirectTile {
 
 // The work item of this workgroup, with every field made explicitly wave-uniform (scalar
 // registers), so that the tensor base pointers derived from it stay in scalar registers.
+// Packed mode: the item's sequence bounds come from the device arrays cu_q / cu_k.
+__device__ __forceinline__ Item varlen_item(const KArgs& a, int g) {
+  Item it;
+  const int T = a.tiles_per_seq;
+  it.t = g % T;
+  const int bh = g / T;
+  it.h = bh % a.H;
+  it.b = bh / a.H;
+  const int q0 = a.cu_q[it.b], k0 = a.cu_k[it.b];
+  it.nq = a.cu_q[it.b + 1] - q0;
+  it.nk = a.cu_k[it.b + 1] - k0;
+  it.diag = it.nk - it.nq;
+  const int rows = a.tiles_over_keys ? it.nk : it.nq;
+  it.valid = it.t * a.tile < rows ? 1 : 0;
+  // -beta * log2(e); the default beta = -ln(nk) gives log2(nk)
+  it.c2 = a.bias ? -a.bias[it.b] * 1.4426950408889634f
+                 : (it.nk > 0 ? __builtin_amdgcn_logf((float)it.nk) : 0.0f);
+  it.qoff = (int64_t)q0 * a.sl + (int64_t)it.h * a.sh;
+  it.koff = (int64_t)k0 * a.sl + (int64_t)it.h * a.sh;
+  it.goff = k0;
+  return it;
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <bool VL>
 __device__ __forceinline__ Item block_item(const KArgs& a) {
-  Item it = decode_item(a, remap_block(blockIdx.x, a.nitems, a.xcd_chunk));
+  const int g = remap_block(blockIdx.x, a.nitems, a.xcd_chunk);
+  Item it = VL ? varlen_item(a, g) : decode_item(a, g);
   it.b = __builtin_amdgcn_readfirstlane(it.b);
   it.h = __builtin_amdgcn_readfirstlane(it.h);
   it.t = __builtin_amdgcn_readfirstlane(it.t);
-  it.n = __builtin_amdgcn_readfirstlane(it.n);
+  it.nq = __builtin_amdgcn_readfirstlane(it.nq);
+  it.nk = __builtin_amdgcn_readfirstlane(it.nk);
+  it.diag = __builtin_amdgcn_readfirstlane(it.diag);
+  it.valid = __builtin_amdgcn_readfirstlane(it.valid);
   it.c2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, it.c2)));
+  it.qoff = uniform64(it.qoff);
+  it.koff = uniform64(it.koff);
+  it.goff = uniform64(it.goff);
   return it;
 }
 

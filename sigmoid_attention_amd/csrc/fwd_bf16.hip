@@ -19,7 +19,7 @@
 //
 // Chunk modes (wave-uniform): interior chunks compute every pair; chunks that reach past
 // the valid length, or cross the wave's diagonal under the causal rule, zero the pairs
-// with key >= n or key > query. With a gate, a per-key table in LDS supplies the logit
+// with key >= nk or key > query + diag. With a gate, a per-key table in LDS supplies the logit
 // offset (+inf for padded or dropped keys, which makes P exactly 0) and value factor.
 //
 // With RS the pass also writes the row mass sum_j P_ij of every valid query (the
@@ -62,7 +62,7 @@ struct FwdOcc {
   static constexpr int value = 2;
 };
 
-template <int D, int QB, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool RS>
+template <int D, int QB, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool RS, bool VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<D, QB>::value, FwdOcc<D, QB>::value)))
 void fwd_kernel(const KArgs a) {
   using T = FwdTraits<D, QB, CPT, GATED>;
@@ -72,35 +72,42 @@ void fwd_kernel(const KArgs a) {
   const int l = lane_id(), w = wave_id();
   const int lk = 4 * (l >> 5);
   const SplitSel sel;
-  const Item it = block_item(a);
-  const int n = it.n;
-  const int last = n - 1;
-  const int64_t hoff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
-  const bf16* Qg = (const bf16*)a.q + hoff;
-  const bf16* Kg = (const bf16*)a.k + hoff;
-  const bf16* Vg = (const bf16*)a.v + hoff;
-  const float* Gg = GATED ? a.gate + (int64_t)it.b * a.gsb : nullptr;
+  // VL: packed batch (separate query and key lengths, bottom-right causal diagonal);
+  // otherwise nk = nq and diag = 0 are compile-time facts
+  const Item it = block_item<VL>(a);
+  if (VL && !it.valid) return;
+  const int nq = it.nq, nk = VL ? it.nk : it.nq, diag = VL ? it.diag : 0;
+  const int lastq = nq - 1, lastk = nk - 1;
+  const int64_t koff = VL ? it.koff : it.qoff;
+  const bf16* Qg = (const bf16*)a.q + it.qoff;
+  const bf16* Kg = (const bf16*)a.k + koff;
+  const bf16* Vg = (const bf16*)a.v + koff;
+  const float* Gg = GATED ? a.gate + it.goff : nullptr;
   const int64_t sl = a.sl;
   const int item_q0 = it.t * T::BM;
   const int q0 = item_q0 + w * QB * 32;   // first query of this wave
   const float c1 = a.c1, c2 = it.c2;
 
-  int kend = n;
-  if (CAUSAL) kend = (item_q0 + T::BM < n) ? item_q0 + T::BM : n;
+  // keys of the item: all of them, or (causal) those up to the item's last query + diag
+  int kend = nk;
+  if (CAUSAL) {
+    const int e = (item_q0 + T::BM < nq ? item_q0 + T::BM : nq) + diag;
+    kend = e < 0 ? 0 : (e < nk ? e : nk);
+  }
   const int nch = (kend + 31) / 32;                 // 32-key chunks of the item
   const int ntiles = (nch + CPT - 1) / CPT;
   // chunks this wave computes: none if all its queries are padding; under the causal
-  // rule only chunks holding a key <= its last valid query
-  int wch = q0 < n ? nch : 0;
-  if (CAUSAL && q0 < n) {
-    const int lastq = (q0 + QB * 32 < n ? q0 + QB * 32 : n) - 1;
-    wch = lastq / 32 + 1 < nch ? lastq / 32 + 1 : nch;
+  // rule only chunks holding a key allowed for its last valid query
+  int wch = q0 < nq ? nch : 0;
+  if (CAUSAL && q0 < nq) {
+    const int lk_allowed = (q0 + QB * 32 < nq ? q0 + QB * 32 : nq) - 1 + diag;
+    wch = lk_allowed < 0 ? 0 : (lk_allowed / 32 + 1 < nch ? lk_allowed / 32 + 1 : nch);
   }
 
   auto issue_tile = [&](int t) {
     char* st = smem + (t % T::NSTAGE) * T::STAGE;
-    Tile::load(st, Kg, sl, t * T::BN, last);
-    Tile::load(st + T::TILE, Vg, sl, t * T::BN, last);
+    Tile::load(st, Kg, sl, t * T::BN, lastk);
+    Tile::load(st + T::TILE, Vg, sl, t * T::BN, lastk);
   };
   // gate table of tile t: logit offset in the exp2 domain (+inf drops the key, which
   // gives P = 0 exactly) and value factor, one entry per key, written by wave 0
@@ -108,22 +115,24 @@ void fwd_kernel(const KArgs a) {
     if (GATED && w == 0 && l < T::BN) {
       float* tab = reinterpret_cast<float*>(smem + (t % T::NSTAGE) * T::STAGE + 2 * T::TILE);
       const int key = t * T::BN + l;
-      const float g = Gg[key < last ? key : last];
-      const bool keep = key < n && !(key >= a.gate_sink && g < a.gate_tau);
+      const float g = Gg[key < lastk ? key : lastk];
+      const bool keep = key < nk && !(key >= a.gate_sink && g < a.gate_tau);
       tab[l] = keep ? c2 - __builtin_amdgcn_logf(g + a.gate_eps) : __builtin_inff();
       tab[T::BN + l] = keep ? g : 0.0f;
     }
   };
-  issue_tile(0);
+  if (ntiles > 0) {
+    issue_tile(0);
+    fill_table(0);
+  }
   if (ntiles > 1) issue_tile(1);
-  fill_table(0);
 
   // Q rows as B operands: lane holds query q0 + 32qb + l%32, d = 16ks + 8(l/32) + 0..7.
   bf16x8 qop[QB][T::KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     int row = q0 + 32 * qb + (l & 31);
-    row = row < last ? row : last;
+    row = row < lastq ? row : lastq;
     const bf16* qr = Qg + (int64_t)row * sl + 8 * (l >> 5);
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) qop[qb][ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
@@ -168,10 +177,11 @@ void fwd_kernel(const KArgs a) {
       tc2 = *reinterpret_cast<const f32x4*>(tab + krow + 2 * r0 + lk);
       tg = *reinterpret_cast<const f32x4*>(tab + T::BN + krow + 2 * r0 + lk);
     }
-    // masked chunks keep key <= lim + kb + lk: key < n, and key <= query when causal
-    int lim = n - 1 - kb - lk;
+    // masked chunks keep key <= lim + kb + lk: key < nk, and key <= query + diag when
+    // causal
+    int lim = nk - 1 - kb - lk;
     if (CAUSAL) {
-      const int ld = q0 + 32 * qb + (l & 31) - kb - lk;
+      const int ld = q0 + 32 * qb + (l & 31) + diag - kb - lk;
       lim = ld < lim ? ld : lim;
     }
     float part = 0.0f;
@@ -269,11 +279,15 @@ void fwd_kernel(const KArgs a) {
   // Tiles before `tmask` hold only interior chunks for this wave; the rest run the
   // masked body. Two loops without a mode branch inside; every wave passes the same
   // number of barriers (one per tile).
-  int cfirst = n / 32;                                  // first chunk reaching past n
-  if (CAUSAL) cfirst = (q0 + 1) / 32 < cfirst ? (q0 + 1) / 32 : cfirst;
+  int cfirst = nk / 32;                                 // first chunk reaching past nk
+  if (CAUSAL) {
+    // first chunk holding a key past query q0's last allowed key q0 + diag
+    const int c = q0 + diag + 1 < 0 ? 0 : (q0 + diag + 1) / 32;
+    cfirst = c < cfirst ? c : cfirst;
+  }
   int tmask = cfirst / CPT;
   tmask = tmask < ntiles ? tmask : ntiles;
-  if (q0 >= n) tmask = 0;                               // nothing to compute
+  if (q0 >= nq) tmask = 0;                              // nothing to compute
 
   // One tile. `stage` is the ring slot of tile t: a compile-time constant in the unrolled
   // interior loop (the LDS addresses then fold into immediate offsets), or -1 when it
@@ -321,23 +335,26 @@ void fwd_kernel(const KArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
       mass[qb] += __shfl_xor(mass[qb], 32, 64);
       const int query = q0 + 32 * qb + (l & 31);
-      if (l < 32 && query < n) a.aux[((int64_t)it.b * a.H + it.h) * a.Lmax + query] = mass[qb];
+      if (l < 32 && query < nq) a.aux[((int64_t)it.b * a.H + it.h) * a.Lmax + query] = mass[qb];
     }
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int query = q0 + 32 * qb + (l & 31);
-    if (query < n) {
+    if (query < nq) {
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
-        store_row(a.out0, hoff + (int64_t)query * sl, a.out_f32, acc[qb][dt], 32 * dt, 1.0f);
+        store_row(a.out0, it.qoff + (int64_t)query * sl, a.out_f32, acc[qb][dt], 32 * dt, 1.0f);
     }
   }
 }
 
 template <int D, int QB, int CPT, bool C, bool G, bool SP, bool RS>
 static hipError_t launch_one(const KArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP, RS>), dim3(a.nitems), dim3(256), 0, st, a);
+  if (a.varlen)
+    hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP, false, true>), dim3(a.nitems), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP, RS, false>), dim3(a.nitems), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

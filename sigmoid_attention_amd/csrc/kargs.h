@@ -9,6 +9,13 @@
 // most expensive tiles first. A blockIdx -> item remap then gives each XCD a
 // contiguous chunk of items per round, so that the tiles sharing one head's K/V run on
 // the same XCD and its L2.
+//
+// Packed variable-length batches (device-side cu_seqlens) use a second mode: the grid is
+// B x H x ceil(max_rows / tile) items in (b, h, tile) order with the tile fastest, each
+// workgroup reads its sequence's bounds from device memory and exits at once when its
+// tile starts past the sequence's rows. Query and key lengths may differ; the causal
+// rule is then aligned at the bottom right (key j allowed for query i iff
+// j <= i + nk - nq), which is what a query shard of a longer sequence needs.
 #pragma once
 #include <stdint.h>
 
@@ -49,6 +56,13 @@ struct KArgs {
   float scale;           // s
   float gate_eps;
   float gate_tau;
+  // packed variable-length mode (varlen != 0): the per-batch tables below are unused
+  int32_t varlen;
+  int32_t tiles_per_seq;       // ceil(max rows / tile)
+  int32_t tiles_over_keys;     // 1: a pass whose tiles are key rows (dk/dv)
+  const int32_t* cu_q;         // device [B + 1] query row bounds
+  const int32_t* cu_k;         // device [B + 1] key row bounds
+  const float* bias;           // device [B] or null (then beta_b = -ln(nk_b))
   int32_t off[kMaxBatch + 1];  // prefix item counts by sorted position
   float c2[kMaxBatch];         // -beta * log2(e) by sorted position
   uint16_t len[kMaxBatch];     // valid length by sorted position
@@ -56,11 +70,17 @@ struct KArgs {
 };
 
 struct Item {
-  int b;      // batch index
-  int h;      // head
-  int t;      // tile index (rows t*tile .. t*tile+tile-1)
-  int n;      // valid length of batch entry b
-  float c2;   // -beta_b * log2(e)
+  int b;         // batch index
+  int h;         // head
+  int t;         // tile index (rows t*tile .. t*tile+tile-1)
+  int nq;        // query rows of this sequence
+  int nk;        // key rows of this sequence
+  int diag;      // causal: key j allowed for query i iff j <= i + diag
+  int valid;     // 0: the item lies past its sequence (packed mode only)
+  float c2;      // -beta_b * log2(e)
+  int64_t qoff;  // element offset of query row 0 of (b, h) (q, o, dO, dq)
+  int64_t koff;  // element offset of key row 0 of (b, h) (k, v, dk, dv)
+  int64_t goff;  // gate index of key 0 of sequence b
 };
 
 // blockIdx -> item index. Rounds of kNumXcd*chunk items; in each round XCD x (which
@@ -86,9 +106,12 @@ SA_HD inline Item decode_item(const KArgs& a, int g) {
   Item it;
   const int p = lo;
   it.b = a.bidx[p];
-  it.n = a.len[p];
+  const int n = a.len[p];
+  it.nq = it.nk = n;
+  it.diag = 0;
+  it.valid = 1;
   it.c2 = a.c2[p];
-  const int T = (it.n + a.tile - 1) / a.tile;
+  const int T = (n + a.tile - 1) / a.tile;
   const int local = g - a.off[p];
   if (a.causal) {
     it.h = local % a.H;
@@ -98,6 +121,8 @@ SA_HD inline Item decode_item(const KArgs& a, int g) {
     it.t = local % T;
   }
   if (a.reverse) it.t = T - 1 - it.t;
+  it.qoff = it.koff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
+  it.goff = (int64_t)it.b * a.gsb;
   return it;
 }
 

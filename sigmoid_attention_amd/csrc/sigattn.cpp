@@ -105,9 +105,11 @@ sigattn_status check_tensors(const void* const* in, int nin, void* const* out, i
   return SIGATTN_OK;
 }
 
-int tile_rows(const sigattn_problem* p, int pass) {
-  return pass == 0 ? sa::fwd_tile_rows(p->d) : pass == 1 ? sa::dq_tile_rows(p->d) : sa::dkdv_tile_rows(p->d);
+int tile_rows_d(int d, int pass) {
+  return pass == 0 ? sa::fwd_tile_rows(d) : pass == 1 ? sa::dq_tile_rows(d) : sa::dkdv_tile_rows(d);
 }
+
+int tile_rows(const sigattn_problem* p, int pass) { return tile_rows_d(p->d, pass); }
 
 int xcd_chunk_default() {
   static int v = [] {
@@ -255,6 +257,79 @@ sigattn_status check_plane(const void* plane, const void* const* others, int not
   return SIGATTN_OK;
 }
 
+// ---------------------------------- packed batches ----------------------------------
+
+sigattn_status validate_varlen(const sigattn_varlen* p) {
+  if (!p) return SIGATTN_ERR_INVALID_ARG;
+  if (p->struct_size != sizeof(sigattn_varlen)) return SIGATTN_ERR_INVALID_ARG;
+  if (p->B < 0 || p->H < 1 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0)
+    return SIGATTN_ERR_INVALID_ARG;
+  if (p->d != 64 && p->d != 128) return SIGATTN_ERR_UNSUPPORTED;
+  if (p->out_dtype != SIGATTN_BF16 && p->out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
+  if (p->fast_math != 0 && p->fast_math != 1) return SIGATTN_ERR_INVALID_ARG;
+  if (p->causal != 0 && p->causal != 1) return SIGATTN_ERR_INVALID_ARG;
+  if (p->stride_t < 0 || p->stride_h < 0) return SIGATTN_ERR_INVALID_ARG;
+  if (p->stride_t > SIGATTN_MAX_ROW_STRIDE) return SIGATTN_ERR_UNSUPPORTED;
+  if (((p->stride_t * 2) & 15) || ((p->stride_h * 2) & 15)) return SIGATTN_ERR_ALIGNMENT;
+  if (!std::isfinite(p->scale) || p->scale < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+  if (p->B > 0 && (!p->cu_seqlens_q || !p->cu_seqlens_k)) return SIGATTN_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(p->cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(p->cu_seqlens_k) & 3u) ||
+      (reinterpret_cast<uintptr_t>(p->bias) & 3u) || (reinterpret_cast<uintptr_t>(p->gate) & 3u))
+    return SIGATTN_ERR_ALIGNMENT;
+  if (p->gate) {
+    if (!std::isfinite(p->gate_eps) || p->gate_eps < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(p->gate_tau) || p->gate_tau < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+    if (p->gate_sink < 0) return SIGATTN_ERR_INVALID_ARG;
+  }
+  for (int pass = 0; pass < 3; ++pass) {
+    const int64_t rows = pass == 2 ? p->max_seqlen_k : p->max_seqlen_q;
+    const int tile = pass == 0 ? sa::fwd_tile_rows(p->d) : pass == 1 ? sa::dq_tile_rows(p->d)
+                                                                    : sa::dkdv_tile_rows(p->d);
+    if ((int64_t)p->B * p->H * ((rows + tile - 1) / tile) > 0x7fffffffLL)
+      return SIGATTN_ERR_UNSUPPORTED;
+  }
+  return SIGATTN_OK;
+}
+
+sigattn_status run_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k,
+                          const void* v, const void* dout, void* o0, void* o1, void* stream) {
+  KArgs a;
+  std::memset(&a, 0, sizeof(a));
+  const int tile = tile_rows_d(p->d, pass);
+  const int64_t rows = pass == 2 ? p->max_seqlen_k : p->max_seqlen_q;
+  a.varlen = 1;
+  a.tile = tile;
+  a.tiles_per_seq = (int32_t)((rows + tile - 1) / tile);
+  a.tiles_over_keys = pass == 2 ? 1 : 0;
+  a.nitems = (int32_t)((int64_t)p->B * p->H * a.tiles_per_seq);
+  if (a.nitems == 0) return SIGATTN_OK;
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_k = p->cu_seqlens_k;
+  a.bias = p->bias;
+  a.H = p->H;
+  a.xcd_chunk = xcd_chunk_default();
+  a.causal = p->causal;
+  a.sl = p->stride_t;
+  a.sh = p->stride_h;
+  const double s = p->scale != 0.0f ? (double)p->scale : 1.0 / std::sqrt((double)p->d);
+  a.scale = (float)s;
+  a.c1 = (float)(-s * kLog2eD);
+  a.gate = p->gate;
+  a.gate_eps = p->gate_eps;
+  a.gate_tau = p->gate_tau;
+  a.gate_sink = p->gate_sink;
+  a.out_f32 = p->out_dtype == SIGATTN_F32 ? 1 : 0;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool causal = p->causal != 0, gated = p->gate != nullptr, split = p->fast_math == 0;
+  hipError_t e;
+  if (pass == 0) e = sa::launch_fwd_bf16(a, p->d, causal, gated, split, st);
+  else if (pass == 1) e = sa::launch_dq_bf16(a, p->d, causal, gated, split, st);
+  else e = sa::launch_dkdv_bf16(a, p->d, causal, gated, split, st);
+  return e == hipSuccess ? SIGATTN_OK : SIGATTN_ERR_HIP;
+}
+
 // ------------------------------------ KV cache ------------------------------------
 
 constexpr int64_t kMaxCacheCap = int64_t(1) << 24;
@@ -377,6 +452,37 @@ sigattn_status sigattn_bwd_dkdv_dg(const sigattn_problem* p, const void* q, cons
     if ((s = check_plane(dg, others2, 8)) != SIGATTN_OK) return s;
   }
   return run_pass(p, 2, q, k, v, dout, dk, dv, stream, dg_head, dg);
+}
+
+sigattn_status sigattn_fwd_varlen(const sigattn_varlen* p, const void* q, const void* k,
+                                  const void* v, void* o, void* stream) {
+  sigattn_status s = validate_varlen(p);
+  if (s != SIGATTN_OK) return s;
+  const void* in[3] = {q, k, v};
+  void* out[1] = {o};
+  if ((s = check_tensors(in, 3, out, 1)) != SIGATTN_OK) return s;
+  return run_varlen(p, 0, q, k, v, nullptr, o, nullptr, stream);
+}
+
+sigattn_status sigattn_bwd_dq_varlen(const sigattn_varlen* p, const void* q, const void* k,
+                                     const void* v, const void* dout, void* dq, void* stream) {
+  sigattn_status s = validate_varlen(p);
+  if (s != SIGATTN_OK) return s;
+  const void* in[4] = {q, k, v, dout};
+  void* out[1] = {dq};
+  if ((s = check_tensors(in, 4, out, 1)) != SIGATTN_OK) return s;
+  return run_varlen(p, 1, q, k, v, dout, dq, nullptr, stream);
+}
+
+sigattn_status sigattn_bwd_dkdv_varlen(const sigattn_varlen* p, const void* q,
+                                       const void* k, const void* v, const void* dout,
+                                       void* dk, void* dv, void* stream) {
+  sigattn_status s = validate_varlen(p);
+  if (s != SIGATTN_OK) return s;
+  const void* in[4] = {q, k, v, dout};
+  void* out[2] = {dk, dv};
+  if ((s = check_tensors(in, 4, out, 2)) != SIGATTN_OK) return s;
+  return run_varlen(p, 2, q, k, v, dout, dk, dv, stream);
 }
 
 sigattn_status sigattn_cache_build(const sigattn_cache* c, const sigattn_problem* p,

@@ -288,3 +288,57 @@ def test_cache_build_checks(lib):
     p.dtype = 1
     p.out_dtype = 1
     assert f(ctypes.byref(c), ctypes.byref(p), k, v, None) == 2
+
+
+def _varlen(**kw):
+    p = S.VarlenDesc()
+    p.struct_size = ctypes.sizeof(S.VarlenDesc)
+    p.B, p.H, p.d = 3, 2, 64
+    p.max_seqlen_q, p.max_seqlen_k = 100, 200
+    p.out_dtype, p.fast_math = 0, 0
+    p.stride_t, p.stride_h = 128, 64
+    p.cu_seqlens_q, p.cu_seqlens_k = 1 << 20, (1 << 20) + 64
+    p.causal, p.scale = 0, 0.0
+    p.gate_eps, p.gate_tau, p.gate_sink = 1e-8, 0.0, 4
+    for key, val in kw.items():
+        setattr(p, key, val)
+    return p
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda p: setattr(p, "d", 80), 2),
+    (lambda p: setattr(p, "H", 0), 1),
+    (lambda p: setattr(p, "max_seqlen_q", -1), 1),
+    (lambda p: setattr(p, "out_dtype", 4), 2),
+    (lambda p: setattr(p, "causal", 3), 1),
+    (lambda p: setattr(p, "stride_t", 100), 3),
+    (lambda p: setattr(p, "stride_t", (1 << 22) + 8), 2),
+    (lambda p: setattr(p, "cu_seqlens_q", None), 1),
+    (lambda p: setattr(p, "cu_seqlens_k", (1 << 20) + 2), 3),
+    (lambda p: setattr(p, "scale", -2.0), 1),
+    (lambda p: (setattr(p, "gate", 1 << 24), setattr(p, "gate_tau", -1.0)), 1),
+    (lambda p: (setattr(p, "B", 1 << 20), setattr(p, "H", 64), setattr(p, "max_seqlen_k", 1 << 20)), 2),
+    (lambda p: setattr(p, "struct_size", 8), 1),
+])
+def test_varlen_validation_before_launch(lib, mutate, code):
+    """Packed-batch entry points validate the description first (fake device pointers:
+    nothing may be enqueued)."""
+    p = _varlen()
+    mutate(p)
+    vp = ctypes.c_void_p
+    t = [vp((1 << 21) * (i + 1)) for i in range(6)]
+    assert lib.sigattn_fwd_varlen(ctypes.byref(p), t[0], t[1], t[2], t[3], None) == code
+    assert lib.sigattn_bwd_dq_varlen(ctypes.byref(p), t[0], t[1], t[2], t[3], t[4], None) == code
+    assert lib.sigattn_bwd_dkdv_varlen(ctypes.byref(p), t[0], t[1], t[2], t[3], t[4], t[5],
+                                       None) == code
+
+
+def test_varlen_output_checks(lib):
+    p = _varlen()
+    vp = ctypes.c_void_p
+    q, k, v = vp(1 << 21), vp(1 << 22), vp(1 << 23)
+    assert lib.sigattn_fwd_varlen(ctypes.byref(p), q, k, v, q, None) == 1       # o aliases q
+    assert lib.sigattn_fwd_varlen(ctypes.byref(p), q, k, v, None, None) == 1
+    assert lib.sigattn_fwd_varlen(ctypes.byref(p), vp((1 << 21) + 4), k, v, vp(1 << 24), None) == 3
+    two = vp(1 << 25)
+    assert lib.sigattn_bwd_dkdv_varlen(ctypes.byref(p), q, k, v, q, two, two, None) == 1
