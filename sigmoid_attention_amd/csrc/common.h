@@ -318,14 +318,15 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {
 // bf16(v - hi), so that hi + lo carries about 16 significant bits. The residual
 // v - hi is exact in float and is formed by one v_dot2c_f32_bf16 per element:
 // v + (hi0, hi1) . (-1, 0).
-// The two selector pairs (-1, 0) and (0, -1) live in registers, built once per kernel
-// from their bit patterns 0x0000bf80 and 0xbf800000: as an inline-constant operand of a
-// packed bf16 instruction they would not carry the intended halves.
+// The two selector pairs (-1, 0) and (0, -1) live in scalar registers (the instruction
+// takes its first source from one), built once per kernel from their bit patterns
+// 0x0000bf80 and 0xbf800000: as an inline-constant operand of a packed bf16 instruction
+// they would not carry the intended halves.
 struct SplitSel {
   bf16x2 m0, m1;
   __device__ __forceinline__ SplitSel() {
     uint32_t b0 = 0x0000bf80u, b1 = 0xbf800000u;
-    asm volatile("" : "+v"(b0), "+v"(b1));
+    asm volatile("" : "+s"(b0), "+s"(b1));
     m0 = __builtin_bit_cast(bf16x2, b0);
     m1 = __builtin_bit_cast(bf16x2, b1);
   }

@@ -12,8 +12,7 @@
 //
 // Per 32-key chunk c a wave runs a software pipeline: the MFMAs of S(c+1) are issued
 // while the VALU evaluates the logistic function of S(c) (computed one chunk earlier), and
-// the P V MFMAs of each 8-key group follow the VALU work of that group, interleaved with
-// the next group's VALU work. At d = 64 the two transcendentals per pair (exp2, rcp; a
+// the P V MFMAs of each 16-key half follow the VALU work of that half. At d = 64 the two transcendentals per pair (exp2, rcp; a
 // quarter of the FMA rate on gfx950) cost about as much as the two products, so keeping
 // both pipes busy at once is what sets the speed.
 //
@@ -52,18 +51,18 @@ enum ChunkMode { kInterior = 0, kMasked = 1 };
 // Register row (within a 32-row MFMA result) of entry r, without the lane term 4*(l/32).
 __device__ __forceinline__ constexpr int arc(int r) { return 8 * (r >> 2) + (r & 3); }
 
-// Waves per SIMD the register budget is sized for: 3 when each wave holds one 32-query
-// block at d = 64, else 2.
+// Waves per SIMD the register budget is sized for: 3 at d = 64 (168 registers, which the
+// unit without the deferred half fits), 2 at d = 128 and for the row-mass variant.
 #ifndef SA_FWD64_QB
 #define SA_FWD64_QB 1
 #endif
-template <int D, int QB>
+template <int D, int QB, bool RS>
 struct FwdOcc {
-  static constexpr int value = 2;
+  static constexpr int value = (D == 64 && !RS) ? 3 : 2;
 };
 
 template <int D, int QB, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool RS, bool VL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<D, QB>::value, FwdOcc<D, QB>::value)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<D, QB, RS>::value, FwdOcc<D, QB, RS>::value)))
 void fwd_kernel(const KArgs a) {
   using T = FwdTraits<D, QB, CPT, GATED>;
   using Tile = DirectTile<T::BN, D, T::kWaves>;
@@ -201,78 +200,67 @@ void fwd_kernel(const KArgs a) {
     else ph = pack8(p, 8 * h);
   };
 
-  // P V of the second key half (h = 1) of a unit is deferred into the next unit, with
-  // its bf16 operands and V operands carried in registers (zero before the first unit,
-  // flushed after the last). Program order is fixed by scheduling barriers into steps
-  // that pair VALU work with MFMAs that do not depend on it; the K and V operand reads
-  // are issued first so that their latency hides behind the first VALU steps:
-  //   1: logistic of entries 0-3           | deferred P V (h = 1 of the previous unit)
-  //   2: entries 4-7, to bf16 (h = 0)      |   "          second half of d
-  //   3: entries 8-11                      | S(u+1), first half of the k-steps
-  //   4: entries 12-15, to bf16 (h = 1)    | S(u+1), second half; P V (h = 0)
-  bf16x8 dph = {}, dpl = {}, dvop[T::DT];
-#pragma unroll
-  for (int dt = 0; dt < T::DT; ++dt) dvop[dt] = bf16x8{};
-  int dqb = 0;
   auto pv = [&](int qb, int dt, const bf16x8& vo, const bf16x8& hi, const bf16x8& lo) {
     acc[qb][dt] = mfma(vo, hi, acc[qb][dt]);
     if (SPLIT) acc[qb][dt] = mfma(vo, lo, acc[qb][dt]);
   };
 
+  // One unit (query block qb against one 32-key chunk). Program order is fixed by
+  // scheduling barriers into steps that pair VALU work with MFMAs that do not depend on
+  // it; the K and V operand reads are issued first so that their latency hides behind the
+  // first VALU step. Nothing is carried into the next unit but S(u+1); the second key
+  // half's P V closes the unit and overlaps the VALU work of the other waves on the SIMD
+  // (three at d = 64):
+  //   1: logistic of entries 0-3           | S(u+1), first half of the k-steps
+  //   2: entries 4-7, to bf16 (h = 0)      | S(u+1), second half
+  //   3: entries 8-11                      | P V (h = 0)
+  //   4: entries 12-15, to bf16 (h = 1)    | -
+  //   5: -                                 | P V (h = 1)
   const LdsLane<D> lane;
   auto unit = [&](auto mode_tag, int qb, const char* Kn, int kn_row, int qb_next,
-                  const char* Vt, int v_row, const float* tab, int kb) {
+                         const char* Vt, int v_row, const float* tab, int kb) {
     bf16x8 kop[T::KS];
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lane.rowop(Kn, kn_row, ks);
-    bf16x8 vop0[T::DT], vop1[T::DT];
+    bf16x8 vop0[T::DT];
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) vop0[dt] = lane.colop(Vt, v_row, dt);
-#pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) vop1[dt] = lane.colop(Vt, v_row + 16, dt);
     __builtin_amdgcn_sched_barrier(0);
-
     f32x16 p;
     bf16x8 ph0, pl0, ph1, pl1;
     f32x16 s_next = zero16();
-    // step 1
     sig4(mode_tag, qb, 0, kb, tab, v_row, p);
-#pragma unroll
-    for (int dt = 0; dt < T::DT / 2; ++dt) pv(dqb, dt, dvop[dt], dph, dpl);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 2
-    sig4(mode_tag, qb, 4, kb, tab, v_row, p);
-    to_bf16(p, 0, ph0, pl0);
-#pragma unroll
-    for (int dt = T::DT / 2; dt < T::DT; ++dt) pv(dqb, dt, dvop[dt], dph, dpl);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 3
-    sig4(mode_tag, qb, 8, kb, tab, v_row, p);
 #pragma unroll
     for (int ks = 0; ks < T::KS / 2; ++ks) s_next = mfma(kop[ks], qop[qb_next][ks], s_next);
     __builtin_amdgcn_sched_barrier(0);
-    // step 4
-    sig4(mode_tag, qb, 12, kb, tab, v_row, p);
-    to_bf16(p, 1, ph1, pl1);
+    sig4(mode_tag, qb, 4, kb, tab, v_row, p);
+    to_bf16(p, 0, ph0, pl0);
 #pragma unroll
     for (int ks = T::KS / 2; ks < T::KS; ++ks) s_next = mfma(kop[ks], qop[qb_next][ks], s_next);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 vop1[T::DT];
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) vop1[dt] = lane.colop(Vt, v_row + 16, dt);
+    sig4(mode_tag, qb, 8, kb, tab, v_row, p);
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) pv(qb, dt, vop0[dt], ph0, pl0);
     __builtin_amdgcn_sched_barrier(0);
-    s_cur = s_next;
-    dph = ph1;
-    dpl = pl1;
+    sig4(mode_tag, qb, 12, kb, tab, v_row, p);
+    to_bf16(p, 1, ph1, pl1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) dvop[dt] = vop1[dt];
-    dqb = qb;
+    for (int dt = 0; dt < T::DT; ++dt) pv(qb, dt, vop1[dt], ph1, pl1);
+    __builtin_amdgcn_sched_barrier(0);
+    s_cur = s_next;
   };
-
   auto chunk = [&](auto mode_tag, const char* Kc, int kc_row, const char* Kn, int kn_row,
                    const char* Vt, int v_row, const float* tab, int kb) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (qb + 1 < QB) unit(mode_tag, qb, Kc, kc_row, qb + 1, Vt, v_row, tab, kb);
-      else unit(mode_tag, qb, Kn, kn_row, 0, Vt, v_row, tab, kb);
+      const char* K1 = qb + 1 < QB ? Kc : Kn;
+      const int k1_row = qb + 1 < QB ? kc_row : kn_row;
+      const int qb1 = qb + 1 < QB ? qb + 1 : 0;
+      unit(mode_tag, qb, K1, k1_row, qb1, Vt, v_row, tab, kb);
     }
   };
 
@@ -324,10 +312,6 @@ void fwd_kernel(const KArgs a) {
   }
   for (; t < tmask; ++t) tile_body(Int{}, Dyn{}, t);
   for (; t < ntiles; ++t) tile_body(Msk{}, Dyn{}, t);
-
-  // the deferred half of the last unit
-#pragma unroll
-  for (int dt = 0; dt < T::DT; ++dt) pv(dqb, dt, dvop[dt], dph, dpl);
 
   // epilogue: valid query rows only (rows >= n are zero-filled by a separate kernel)
   if (RS) {
