@@ -264,12 +264,15 @@ void dkdv_kernel(const KArgs a) {
   };
 
   // Tile loops: [t0, tm1) masked (the causal diagonal chunk), [tm1, tm2) interior,
-  // [tm2, ntiles) masked (the chunk holding the last valid query when nq % 32 != 0).
+  // [tm2, ntiles) masked (the tile holding the last valid query when nq % 32 != 0 or
+  // when it holds fewer than CPT chunks).
   // Every wave passes one barrier per tile.
   // masked under the causal rule: chunks up to the one holding query k0 + 31 - diag
   int tm1 = t0;
   if (CAUSAL && k0 + 31 - diag >= 0) tm1 = (k0 + 31 - diag) / 32 / CPT + 1;
-  int tm2 = (nq % 32 != 0) ? (nch - 1) / CPT : ntiles;
+  // the tile holding the last query chunk is masked when that chunk is partial or when
+  // the tile reaches past the last chunk (nch not a multiple of CPT)
+  int tm2 = (nq % 32 != 0 || nch % CPT != 0) ? (nch - 1) / CPT : ntiles;
   if (c_lo >= nch) { tm1 = ntiles; tm2 = ntiles; }
   tm1 = tm1 < ntiles ? tm1 : ntiles;
   tm2 = tm2 > tm1 ? tm2 : tm1;

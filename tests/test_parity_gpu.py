@@ -71,6 +71,21 @@ def test_small_full_parity(d, variant):
     print(check_bounds(gpu, ref, mag, data["seqlens"], True, True, f"small {variant} {d} fast"))
 
 
+@pytest.mark.parametrize("variant", ["bidir", "causal_gated_drop"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_lengths_at_chunk_multiples(d, variant):
+    """Lengths that are exact multiples of the 32-row chunk, odd and even numbers of them
+    (a tile of two chunks is then half valid), next to 1 and 64 + 1; full comparison."""
+    torch = need_gpu()
+    w = W.Workload(f"chunk_mult_{variant}_{d}", "bf16", 7, 2, d, 300,
+                   ("fixed", [96, 32, 160, 288, 64, 1, 65]), seed=31 + d,
+                   **SMALL_VARIANTS[variant])
+    data = W.generate(w)
+    note(f"chunk-multiple lengths d={d} {variant}")
+    gpu = run_gpu(data, torch.bfloat16, out_dtype=torch.float32)
+    print(check_all(gpu, oracle_full(data), data["seqlens"], BF16_TOL, f"chunks {variant} {d}"))
+
+
 @pytest.mark.parametrize("name", ["causal_gated_512", "causal_forced_drop_512"])
 def test_causal_gated_full(name):
     """Causal GPT-2-shaped gated layer (B=16, H=12, d=64, L=512) against the full oracle."""
