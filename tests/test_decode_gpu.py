@@ -54,7 +54,7 @@ def _assert_same_cache(gpu, ref, label):
 
 def _small(d, gated, lens=(300, 0, 1, 3, 257, 512), cap=600, seed=0):
     gate = ("logistic_normal", 1.0, 2.0, 0.3, 0.01) if gated else None
-    w = W.Workload(f"dec_small_{d}_{int(gated)}", "bf16", len(lens), 3, d, 512,
+    w = W.Workload(f"dec_small_{d}_{int(gated)}", "bf16", len(lens), 3, d, max(512, max(lens)),
                    ("fixed", list(lens)), seed=300 + d + seed, gate=gate,
                    tau=0.05 if gated else 0.0, sink=4, extra={"cap": cap})
     return W.generate_decode(w)
@@ -203,4 +203,29 @@ def test_decode_workloads(name):
         gots.append(got[b])
     e = err_ratio(np.stack(gots), np.stack(refs), np.ones((len(picks), H, d), bool))
     print(f"{name}: ratio {e:.3e}, live fraction {counts.sum() / (sl.sum() + B):.3f}")
+    assert e <= BF16_TOL
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_counts_around_chunk_edges(d, gated):
+    """Cache lengths around the decode's 16-row steps, 128-row wave slices and 512-row
+    chunks (1, 15, 16, 17, 127, 128, 129, 511, 512, 513, 1000, 1024 prefill positions)."""
+    torch = need_gpu()
+    data = _small(d, gated, lens=(1, 15, 16, 17, 127, 128, 129, 511, 512, 513, 1000, 1024),
+                  cap=1100, seed=7)
+    cache = _make_cache(torch, data, d)
+    gate_t = None if data["gate"] is None else _dev(torch, data["gate"])
+    note(f"decode chunk edges d={d} gated={gated}")
+    cache.build(_dev(torch, data["k"], torch.bfloat16), _dev(torch, data["v"], torch.bfloat16),
+                data["seqlens"], gate=gate_t)
+    ref = _oracle_cache(data, data["cap"])
+    _assert_same_cache(_gpu_cache_state(cache), ref, "build")
+    bias = [-math.log(int(n)) for n in data["seqlens"]]
+    out = cache.decode(_dev(torch, data["q"], torch.bfloat16), bias, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = O.decode(data["q"], ref[0], ref[1], ref[2], ref[3], bias)
+    e = err_ratio(got, want, np.ones(got.shape, bool))
+    print(f"decode chunk edges ratio {e:.3e}")
     assert e <= BF16_TOL

@@ -84,3 +84,20 @@ def test_strided_blhd_views(d):
     gpu = {"O": o.cpu().numpy(), "dQ": dq.cpu().numpy(), "dK": dk.cpu().numpy(),
            "dV": dv.cpu().numpy()}
     print(check_all(gpu, ref, sl, BF16_TOL, f"BLHD d={d}"))
+
+
+@pytest.mark.parametrize("variant", ["bidir", "causal", "causal_gated_drop"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_every_length_up_to_256(d, variant):
+    """One batch holding every length 1..256 (every residue modulo the 32-row chunk and
+    the 128-row tile, odd and even chunk counts), all passes against the oracle."""
+    torch = need_gpu()
+    kw = {"bidir": dict(), "causal": dict(causal=True),
+          "causal_gated_drop": dict(causal=True, gate=("logistic_normal", 2.0, 2.0, 0.3, 0.01),
+                                    tau=0.05, sink=4)}[variant]
+    w = W.Workload(f"every_len_{variant}_{d}", "bf16", 256, 1, d, 256,
+                   ("fixed", list(range(1, 257))), seed=530 + d, **kw)
+    data = W.generate(w)
+    note(f"every length 1..256 d={d} {variant}")
+    gpu = run_gpu(data, torch.bfloat16, out_dtype=torch.float32)
+    print(check_all(gpu, oracle_full(data), data["seqlens"], BF16_TOL, f"every length {d} {variant}"))

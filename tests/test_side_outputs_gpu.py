@@ -257,3 +257,19 @@ def test_row_mass_long_sampled():
     print("long row mass sampled ratio", e)
     assert e <= BF16_TOL
     assert np.array_equal(gpu["O"], gpu["O0"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_side_outputs_every_length(d):
+    """Gate gradient and row mass on one batch holding every length 1..256, causal with
+    dropped keys."""
+    torch = need_gpu()
+    w = W.Workload(f"side_every_{d}", "bf16", 256, 1, d, 256, ("fixed", list(range(1, 257))),
+                   seed=560 + d, causal=True, gate=("logistic_normal", 2.0, 2.0, 0.3, 0.01),
+                   tau=0.05, sink=4)
+    data = W.generate(w)
+    note(f"side outputs, every length 1..256, d={d}")
+    print(_check(_gpu_dg(data, torch, torch.bfloat16, out_dtype=torch.float32), data,
+                 label=f"dg every {d}"))
+    print(_check_rm(_gpu_rm(data, torch, torch.bfloat16, out_dtype=torch.float32), data,
+                    label=f"rm every {d}"))

@@ -142,3 +142,18 @@ def test_context_parallel_shard(causal):
         for name, ref in (("O", o), ("dQ", dq)):
             e = err_ratio(gpu[name][rows, h], ref, np.ones(ref.shape, bool))
             assert e <= BF16_TOL, f"shard {name} head {h}: {e:.3e}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_length_grid(d, causal):
+    """Every pair of query and key lengths from a grid around the 32-row chunk and the
+    128-row tile (196 sequences, more queries than keys and the reverse)."""
+    torch = need_gpu()
+    grid = [1, 31, 32, 33, 63, 64, 65, 95, 96, 127, 128, 129, 160, 200]
+    lq = [a for a in grid for _ in grid]
+    lk = [b for _ in grid for b in grid]
+    c = _packed_case(430 + d + causal, lq, lk, 1, d)
+    note(f"varlen length grid d={d} causal={causal}")
+    gpu = _run(torch, c, causal)
+    print(_check(gpu, c, causal, label=f"grid {d} {causal}"))
