@@ -15,14 +15,14 @@
 //  * decode: o = sum_j sigma(s q . k_j + beta [+ log(g_j + eps)]) [g_j] v_j over the live
 //    entries. One query against a stream of cache rows is a matrix-vector product: it is
 //    bound by HBM bandwidth, not by the matrix cores, so it runs on the vector ALUs. Each
-//    cache row is read by d/16 lanes, 16 B per load (each load instruction covers
-//    contiguous 64 B or 128 B row halves); the dot product uses v_dot2_f32_bf16 and a
-//    butterfly over the row's lanes; four steps of loads are issued before their math so
-//    that enough bytes are in flight. The rows of one (b, h) are split into chunks of
-//    512 entries, one workgroup each, so that the work is even whatever the cache
-//    lengths; a chunk's partial sum of weighted values is a plain sum (no row maximum or
-//    normaliser to merge, unlike softmax), written to a workspace and added up in chunk
-//    order by a second kernel: deterministic, no atomics.
+//    cache row is read by 8 lanes with non-temporal 16-byte loads, so that each load
+//    instruction covers whole 128-byte lines (a streamed row is never read again); the
+//    dot product uses v_dot2_f32_bf16 and a butterfly over the row's lanes; eight steps
+//    of loads are issued before their math so that enough bytes are in flight. The rows
+//    of one (b, h) are split into chunks of 512 entries, one workgroup each, so that the
+//    work is even whatever the cache lengths; a chunk's partial sum of weighted values is
+//    a plain sum (no row maximum or normaliser to merge, unlike softmax), written to a
+//    workspace and added up in chunk order by a second kernel: deterministic, no atomics.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -146,6 +146,13 @@ __device__ __forceinline__ int live_count(const CacheView& c, int b) {
   return m < 0 ? 0 : (m > c.cap ? c.cap : m);
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// 16 bytes of a cache row, which is read once per decode: a non-temporal load
+__device__ __forceinline__ bf16x8 stream_load(const bf16* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 template <int I>
 __device__ __forceinline__ bf16x2 pair(const bf16x8& v) {
   return __builtin_shufflevector(v, v, 2 * I, 2 * I + 1);
@@ -161,9 +168,10 @@ __device__ __forceinline__ float dot8(const bf16x8& a, const bf16x8& b, float ac
 
 template <int D, bool GATED>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
-  constexpr int LPK = D / 16;              // lanes per cache row (16 features each)
+  constexpr int LPK = 8;                   // lanes per cache row
+  constexpr int NL = D / 64;               // 16-byte loads per lane and row (one per 128 B)
   constexpr int KPS = 64 / LPK;            // rows per wave step
-  constexpr int U = 4;                     // steps whose loads are issued together
+  constexpr int U = 8;                     // steps whose loads are issued together
   constexpr int KPW = kDecChunk / 4;       // rows per wave and chunk
   constexpr int NIT = KPW / (U * KPS);
   static_assert(NIT * U * KPS == KPW, "chunk must split into whole iterations");
@@ -177,10 +185,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 
   const int l = lane_id(), w = wave_id();
   const int ks = l / LPK, sub = l % LPK;
-  // this lane's features: 8 sub .. 8 sub + 7 and D/2 + 8 sub .. D/2 + 8 sub + 7
-  const bf16* qp = (const bf16*)a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh;
-  const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qp + 8 * sub);
-  const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qp + D / 2 + 8 * sub);
+  // this lane's features: 64 i + 8 sub .. 64 i + 8 sub + 7 for i < NL, so that each load
+  // instruction of a wave covers whole 128-byte lines of its rows
+  const bf16* qp = (const bf16*)a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh + 8 * sub;
+  bf16x8 qv[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) qv[i] = *reinterpret_cast<const bf16x8*>(qp + 64 * i);
   const int64_t hoff = (int64_t)b * a.c.sb + (int64_t)h * a.c.sh;
   const bf16* Kb = (const bf16*)a.c.k + hoff + 8 * sub;
   const bf16* Vb = (const bf16*)a.c.v + hoff + 8 * sub;
@@ -189,30 +199,33 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   const int64_t sl = a.c.sl;
   const int last = m - 1;
 
-  float acc[16];
+  float acc[8 * NL];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  for (int e = 0; e < 8 * NL; ++e) acc[e] = 0.0f;
 
   const int wbase = c0 + w * KPW;
   for (int it = 0; it < NIT; ++it) {
     const int jb = wbase + it * U * KPS;
     if (jb >= m) break;   // wave-uniform
-    bf16x8 kr[U][2], vr[U][2];
+    bf16x8 kr[U][NL], vr[U][NL];
     float gv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = jb + u * KPS + ks;
       const int64_t row = (int64_t)(j < last ? j : last) * sl;   // rows past m read row m-1
-      kr[u][0] = *reinterpret_cast<const bf16x8*>(Kb + row);
-      kr[u][1] = *reinterpret_cast<const bf16x8*>(Kb + row + D / 2);
-      vr[u][0] = *reinterpret_cast<const bf16x8*>(Vb + row);
-      vr[u][1] = *reinterpret_cast<const bf16x8*>(Vb + row + D / 2);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        kr[u][i] = stream_load(Kb + row + 64 * i);
+        vr[u][i] = stream_load(Vb + row + 64 * i);
+      }
       if (GATED) gv[u] = Gb[j < last ? j : last];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = jb + u * KPS + ks;
-      float dot = dot8(qb, kr[u][1], dot8(qa, kr[u][0], 0.0f));
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) dot = dot8(qv[i], kr[u][i], dot);
 #pragma unroll
       for (int off = 1; off < LPK; off <<= 1) dot += __shfl_xor(dot, off, 64);
       float t = __builtin_fmaf(dot, c1, c2);
@@ -221,10 +234,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       if (GATED) p *= gv[u];
       p = j < m ? p : 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        acc[e] = __builtin_fmaf(p, (float)vr[u][0][e], acc[e]);
-        acc[8 + e] = __builtin_fmaf(p, (float)vr[u][1][e], acc[8 + e]);
-      }
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[8 * i + e] = __builtin_fmaf(p, (float)vr[u][i][e], acc[8 * i + e]);
     }
   }
 
@@ -232,14 +244,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int off = LPK; off < 64; off <<= 1)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+    for (int e = 0; e < 8 * NL; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
   __shared__ float red[4][D];
   if (ks == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      red[w][8 * sub + e] = acc[e];
-      red[w][D / 2 + 8 * sub + e] = acc[8 + e];
-    }
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[w][64 * i + 8 * sub + e] = acc[8 * i + e];
   }
   __syncthreads();
   const int tid = threadIdx.x;
