@@ -126,6 +126,17 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_problem* p, const void* q, const v
                                 const void* v, const void* dout, void* dk, void* dv,
                                 void* stream);
 
+/* The whole backward in one call: dq as sigattn_bwd_dq, dk and dv as sigattn_bwd_dkdv,
+ * bitwise the same values (the same two kernels' arithmetic; paper: section 4, backward
+ * decomposition, one kernel per side, no atomics). At d = 64 with bf16 inputs both
+ * kernels' work items go into one launch, so that each pass's last, shorter items share
+ * the GPU with the other pass's work instead of leaving it partly idle; otherwise the two
+ * passes are enqueued one after the other. Arguments and errors as for the two calls;
+ * dq, dk and dv must be distinct and alias no input. */
+sigattn_status sigattn_bwd(const sigattn_problem* p, const void* q, const void* k,
+                           const void* v, const void* dout, void* dq, void* dk, void* dv,
+                           void* stream);
+
 /* Backward, key side, plus the gradient of the per-key gate (requires p->gate).
  * g_j enters twice, as log(g_j + eps) on the logits and as the factor g_j on v_j; by the
  * chain rule (diagonal Jacobian as above) the derivative of sum(dO * O) over head h is

@@ -28,7 +28,7 @@ import os
 
 import numpy as np
 
-__all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd_dkdv_dg", "fwd_varlen",
+__all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd", "bwd_dkdv_dg", "fwd_varlen",
            "bwd_dq_varlen", "bwd_dkdv_varlen", "VarlenDesc", "KVCache", "CacheDesc",
            "validate", "plan", "library_path", "load",
            "Problem", "SigattnError", "STATUS", "VERSION"]
@@ -124,6 +124,7 @@ def load():
     lib.sigattn_fwd_rowsum.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.sigattn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dkdv_dg.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     VD = ctypes.POINTER(VarlenDesc)
     lib.sigattn_fwd_varlen.argtypes = [VD, vp, vp, vp, vp, vp]
@@ -321,6 +322,23 @@ def bwd_dkdv(q, k, v, do, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, 
     del keep
     _check(code, "sigattn_bwd_dkdv")
     return dk, dv
+
+
+def bwd(q, k, v, do, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, eps=1e-8,
+        scale=0.0, bias=None, out=None, out_dtype=None, fast_math=False):
+    """(dQ, dK, dV) in one call: the values of bwd_dq and bwd_dkdv, from one launch of both
+    kernels at d = 64."""
+    lib = load()
+    prob, keep = _describe(q, (k, v, do), seqlens, causal, gate, tau, sink, eps, scale, bias,
+                           out_dtype, fast_math)
+    dq, dk, dv = tuple(_new_out(q, out_dtype) for _ in range(3)) if out is None else out
+    for t in (dq, dk, dv):
+        _check_out(q, t, out_dtype)
+    code = lib.sigattn_bwd(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream(q))
+    del keep
+    _check(code, "sigattn_bwd")
+    return dq, dk, dv
 
 
 def _new_plane(q, shape):

@@ -16,8 +16,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsigattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["fwd_bf16.hip", "bwd_dq_bf16.hip", "bwd_dkdv_bf16.hip", "aux_kernels.hip",
-           "decode_bf16.hip", "sigattn.cpp"]
+SOURCES = ["fwd_bf16.hip", "bwd_dq_bf16.hip", "bwd_dkdv_bf16.hip", "bwd_fused_bf16.hip",
+           "aux_kernels.hip", "decode_bf16.hip", "sigattn.cpp"]
 
 # gfx950 only; packed fp32 VALU instructions are disabled (hipcc's host pass warns
 # that it does not know the feature, which is harmless).

@@ -272,10 +272,9 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <bool VL>
-__device__ __forceinline__ Item block_item(const KArgs& a) {
-  const int g = remap_block(blockIdx.x, a.nitems, a.xcd_chunk);
-  Item it = VL ? varlen_item(a, g) : decode_item(a, g);
+// Every field of a work item is the same for the whole workgroup: keep it in scalar
+// registers, so that base pointers built from it do too.
+__device__ __forceinline__ Item uniform_item(Item it) {
   it.b = __builtin_amdgcn_readfirstlane(it.b);
   it.h = __builtin_amdgcn_readfirstlane(it.h);
   it.t = __builtin_amdgcn_readfirstlane(it.t);
@@ -288,6 +287,12 @@ __device__ __forceinline__ Item block_item(const KArgs& a) {
   it.koff = uniform64(it.koff);
   it.goff = uniform64(it.goff);
   return it;
+}
+
+template <bool VL>
+__device__ __forceinline__ Item block_item(const KArgs& a) {
+  const int g = remap_block(blockIdx.x, a.nitems, a.xcd_chunk);
+  return uniform_item(VL ? varlen_item(a, g) : decode_item(a, g));
 }
 
 // Wait until every vector-memory operation of this wave has completed (including direct

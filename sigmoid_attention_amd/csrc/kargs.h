@@ -96,7 +96,8 @@ SA_HD inline int remap_block(int w, int nitems, int chunk) {
   return (s / chunk) * round + x * chunk + (s % chunk);
 }
 
-SA_HD inline Item decode_item(const KArgs& a, int g) {
+// `reverse` lists a sequence's tiles last-first (the causal query-side passes).
+SA_HD inline Item decode_item(const KArgs& a, int g, int reverse) {
   // largest p with off[p] <= g (off is non-decreasing, off[0] = 0)
   int lo = 0, hi = a.nsorted - 1;
   while (lo < hi) {
@@ -120,10 +121,12 @@ SA_HD inline Item decode_item(const KArgs& a, int g) {
     it.h = local / T;
     it.t = local % T;
   }
-  if (a.reverse) it.t = T - 1 - it.t;
+  if (reverse) it.t = T - 1 - it.t;
   it.qoff = it.koff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
   it.goff = (int64_t)it.b * a.gsb;
   return it;
 }
+
+SA_HD inline Item decode_item(const KArgs& a, int g) { return decode_item(a, g, a.reverse); }
 
 }  // namespace sa

@@ -21,6 +21,7 @@ namespace sa {
 hipError_t launch_fwd_bf16(const KArgs& a, int d, bool causal, bool gated, bool split, hipStream_t st);
 hipError_t launch_dq_bf16(const KArgs& a, int d, bool causal, bool gated, bool split, hipStream_t st);
 hipError_t launch_dkdv_bf16(const KArgs& a, int d, bool causal, bool gated, bool split, hipStream_t st);
+hipError_t launch_bwd_bf16(const KArgs& a, void* dq, bool causal, bool gated, bool split, hipStream_t st);
 int fwd_tile_rows(int d);
 int dq_tile_rows(int d);
 int dkdv_tile_rows(int d);
@@ -434,6 +435,32 @@ sigattn_status sigattn_bwd_dkdv(const sigattn_problem* p, const void* q, const v
   void* out[2] = {dk, dv};
   if ((s = check_tensors(in, 4, out, 2)) != SIGATTN_OK) return s;
   return run_pass(p, 2, q, k, v, dout, dk, dv, stream);
+}
+
+sigattn_status sigattn_bwd(const sigattn_problem* p, const void* q, const void* k,
+                           const void* v, const void* dout, void* dq, void* dk, void* dv,
+                           void* stream) {
+  sigattn_status s = validate_problem(p);
+  if (s != SIGATTN_OK) return s;
+  const void* in[4] = {q, k, v, dout};
+  void* out[3] = {dq, dk, dv};
+  if ((s = check_tensors(in, 4, out, 3)) != SIGATTN_OK) return s;
+  if (p->B == 0) return SIGATTN_OK;
+  if (p->dtype == SIGATTN_F32 || p->d != 64) {
+    // one kernel after the other (at d = 128 the dK/dV kernel runs one wave per SIMD and
+    // the dQ kernel two, so sharing a launch would hold the dQ items to one)
+    if ((s = run_pass(p, 2, q, k, v, dout, dk, dv, stream)) != SIGATTN_OK) return s;
+    return run_pass(p, 1, q, k, v, dout, dq, nullptr, stream);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  KArgs a;
+  plan_pass(p, 2, &a);
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = dk; a.out1 = dv;
+  if (a.nitems > 0 &&
+      sa::launch_bwd_bf16(a, dq, p->causal != 0, p->gate != nullptr, p->fast_math == 0, st) != hipSuccess)
+    return SIGATTN_ERR_HIP;
+  if ((s = zero_fill(p, dk, dv, st)) != SIGATTN_OK) return s;
+  return zero_fill(p, dq, nullptr, st);
 }
 
 sigattn_status sigattn_bwd_dkdv_dg(const sigattn_problem* p, const void* q, const void* k,

@@ -123,8 +123,16 @@ def test_entry_points_reject_before_launch(lib):
     # dk and dv alias each other
     two = ctypes.c_void_p(1 << 22)
     assert lib.sigattn_bwd_dkdv(ctypes.byref(p), ok, ok, ok, ok, two, two, None) == 1
+    # whole backward: an output aliases another output or an input, a null output
+    three = ctypes.c_void_p(1 << 23)
+    assert lib.sigattn_bwd(ctypes.byref(p), ok, ok, ok, ok, two, two, three, None) == 1
+    assert lib.sigattn_bwd(ctypes.byref(p), ok, ok, ok, ok, two, three, two, None) == 1
+    assert lib.sigattn_bwd(ctypes.byref(p), ok, ok, ok, ok, ok, two, three, None) == 1
+    assert lib.sigattn_bwd(ctypes.byref(p), ok, ok, ok, ok, None, two, three, None) == 1
+    assert lib.sigattn_bwd(ctypes.byref(p), ok, ok, ok, ok, two, three, odd, None) == 3
     # unsupported head size, valid pointers otherwise
     p.d = 80
+    assert lib.sigattn_bwd(ctypes.byref(p), ok, ok, ok, ok, two, three, ctypes.c_void_p(1 << 24), None) == 2
     assert lib.sigattn_bwd_dq(ctypes.byref(p), ok, ok, ok, ok, two, None) == 2
     assert lib.sigattn_fwd(None, ok, ok, ok, two, None) == 1
 
