@@ -1,8 +1,8 @@
 """Benchmark: effective TFLOPS of padded bf16 sigmoid attention (forward + backward) on
 one MI355X, the fp64 CPU oracle timed beside it.
 
-One step = one pass of the whole hot path over one batch: sigattn_fwd, sigattn_bwd_dq
-and sigattn_bwd_dkdv. FLOPs are counted over valid tokens only: 4 d per valid
+One step = one pass of the whole hot path over one batch: sigattn_fwd, then sigattn_bwd
+(the dQ and dK/dV kernels; at d = 64 their work items share one launch). FLOPs are counted over valid tokens only: 4 d per valid
 (query, key) pair forward, 2.5x that backward (the FLOP appendix of "Better Models,
 Faster Training: Sigmoid Attention for single-cell Foundation Models"), n^2 pairs per
 head bidirectional, n(n+1)/2 causal. Inputs are resident in HBM before timing starts.
@@ -32,10 +32,11 @@ sys.path.insert(0, ROOT)
 METRIC = "effective fwd/bwd TFLOPS, bf16 padded sigmoid attn, L=8K; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
-# algorithmic MFMA FLOPs per valid pair, per pass: forward S and P.V (2 x 2d); the dQ pass
-# recomputes S, forms dP and dQ (3 x 2d); the dK/dV pass recomputes S, forms dP, dV, dK
-# (4 x 2d). The credited backward (2.5 x forward = 10 d) counts S and dP once.
-PASS_FLOPS_PER_PAIR = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+# algorithmic MFMA FLOPs per valid pair, per launch: forward S and P.V (2 x 2d); the
+# backward's dQ kernel recomputes S, forms dP and dQ (3 x 2d) and its dK/dV kernel
+# recomputes S, forms dP, dV, dK (4 x 2d): 14 d per pair for the one-call backward. The
+# credited backward (2.5 x forward = 10 d) counts S and dP once.
+PASS_FLOPS_PER_PAIR = {"fwd": 4, "bwd": 14}
 
 
 def parse():
@@ -202,7 +203,8 @@ def measure_decode(S, W, w, steps, warmup, no_cpu, cpu_seconds):
     return res
 
 
-PASS_KERNELS = {"fwd": "fwd_kernel", "bwd_dq": "dq_kernel", "bwd_dkdv": "dkdv_kernel"}
+# kernel names in rocprofv3 output (bwd_kernel: the one-call backward at d = 64)
+PASS_KERNELS = {"fwd": "fwd_kernel", "bwd": "bwd_kernel"}
 DECODE_KERNELS = {"decode": "decode_kernel"}
 COPY_ELEMS = 64 << 20          # float32 elements read and written by the calibration copy
 
@@ -317,8 +319,7 @@ def pmc_pass(S, w, t, gate, sl, out_dtype, fast_math):
               fast_math=fast_math)
     for _ in range(3):
         S.fwd(t["q"], t["k"], t["v"], sl, **kw)
-        S.bwd_dq(t["q"], t["k"], t["v"], t["do"], sl, **kw)
-        S.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], sl, **kw)
+        S.bwd(t["q"], t["k"], t["v"], t["do"], sl, **kw)
     torch.cuda.synchronize()
 
 
@@ -384,7 +385,7 @@ def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False):
     Performance"): sequence length 512..16384 with the batch set so that B * L = 16384
     tokens, head dimension 64 (32 heads) and 128 (16 heads) of a 2048-wide model, 0 % and
     25 % padding; bidirectional. Per configuration the forward and the backward
-    (dQ pass + dK/dV pass) are timed separately, each for `iters` iterations after about
+    (sigattn_bwd: dQ and dK/dV kernels) are timed separately, each for `iters` iterations after about
     `warmup_ms` of warm-up, with a pair of HIP events per iteration on the launch stream;
     TFLOPS count valid tokens only."""
     import torch
@@ -409,8 +410,7 @@ def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False):
                     S.fwd(t["q"], t["k"], t["v"], sl, out=o, **kw)
 
                 def bwd():
-                    S.bwd_dq(t["q"], t["k"], t["v"], t["do"], sl, out=dq, **kw)
-                    S.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], sl, out=(dk, dv), **kw)
+                    S.bwd(t["q"], t["k"], t["v"], t["do"], sl, out=(dq, dk, dv), **kw)
 
                 res = {"L": L, "B": B, "H": H, "d": d, "padding": pad,
                        "seqlens": [int(x) for x in sl]}
@@ -455,18 +455,15 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):
         S.fwd(t["q"], t["k"], t["v"], sl, out=o, **kw)
         if evs is not None:
             evs[1].record(stream)
-        S.bwd_dq(t["q"], t["k"], t["v"], t["do"], sl, out=dq, **kw)
+        S.bwd(t["q"], t["k"], t["v"], t["do"], sl, out=(dq, dk, dv), **kw)
         if evs is not None:
             evs[2].record(stream)
-        S.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], sl, out=(dk, dv), **kw)
-        if evs is not None:
-            evs[3].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -476,17 +473,16 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / steps
-    per = {"fwd": [], "bwd_dq": [], "bwd_dkdv": []}
+    per = {"fwd": [], "bwd": []}
     for e in evs:
         per["fwd"].append(e[0].elapsed_time(e[1]))
-        per["bwd_dq"].append(e[1].elapsed_time(e[2]))
-        per["bwd_dkdv"].append(e[2].elapsed_time(e[3]))
+        per["bwd"].append(e[1].elapsed_time(e[2]))
 
     f_fwd = W.flops_forward(sl, w.H, w.d, w.causal)
     f_bwd = W.flops_backward(sl, w.H, w.d, w.causal)
     pairs = W.valid_pairs(sl, w.causal) * w.H
     fwd_ms = float(np.mean(per["fwd"]))
-    bwd_ms = float(np.mean(per["bwd_dq"])) + float(np.mean(per["bwd_dkdv"]))
+    bwd_ms = float(np.mean(per["bwd"]))
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     kernels = {}
     for name, times in per.items():
@@ -512,13 +508,15 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "Lmax": w.L,
                    "seqlens": [int(x) for x in sl], "causal": w.causal,
                    "gated": w.gate is not None, "seed": w.seed,
-                   "step": "sigattn_fwd + sigattn_bwd_dq + sigattn_bwd_dkdv"},
+                   "step": "sigattn_fwd + sigattn_bwd"},
         "fwd_tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
         "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
         "fwd_pct_peak": 100.0 * f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "bwd_pct_peak": 100.0 * f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "roofline": {"bound": "mfma", "kernel": dom,
+        "roofline": {"bound": "mfma",
+                     "kernel": {"fwd": "fwd_kernel",
+                                "bwd": "bwd_kernel" if w.d == 64 else "dkdv_kernel + dq_kernel"}[dom],
                      "achieved": kernels[dom]["achieved_tflops"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": kernels[dom]["frac_of_peak"],
