@@ -6,6 +6,8 @@ One step = one pass of the whole hot path over one batch: sigattn_fwd, then siga
 (query, key) pair forward, 2.5x that backward (the FLOP appendix of "Better Models,
 Faster Training: Sigmoid Attention for single-cell Foundation Models"), n^2 pairs per
 head bidirectional, n(n+1)/2 causal. Inputs are resident in HBM before timing starts.
+The two backward passes are also timed alone, outside the timed step (sigattn_bwd_dq and
+sigattn_bwd_dkdv under "kernels").
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_8k_s1]
                     [--no-cpu-baseline]
@@ -36,7 +38,7 @@ PEAK_HBM_GBS = 8000.0
 # backward's dQ kernel recomputes S, forms dP and dQ (3 x 2d) and its dK/dV kernel
 # recomputes S, forms dP, dV, dK (4 x 2d): 14 d per pair for the one-call backward. The
 # credited backward (2.5 x forward = 10 d) counts S and dP once.
-PASS_FLOPS_PER_PAIR = {"fwd": 4, "bwd": 14}
+PASS_FLOPS_PER_PAIR = {"fwd": 4, "bwd": 14, "bwd_dq": 6, "bwd_dkdv": 8}
 
 
 def parse():
@@ -478,6 +480,22 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):
         per["fwd"].append(e[0].elapsed_time(e[1]))
         per["bwd"].append(e[1].elapsed_time(e[2]))
 
+    # each backward pass alone as well (outside the timed step): the two kernels that the
+    # one-call backward runs in one launch
+    sep = {"bwd_dq": lambda: S.bwd_dq(t["q"], t["k"], t["v"], t["do"], sl, out=dq, **kw),
+           "bwd_dkdv": lambda: S.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], sl, out=(dk, dv), **kw)}
+    for name, fn in sep.items():
+        for _ in range(max(2, warmup // 4)):
+            fn()
+        pairs_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in range(steps)]
+        for e0, e1 in pairs_ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        per[name] = [e0.elapsed_time(e1) for e0, e1 in pairs_ev]
+
     f_fwd = W.flops_forward(sl, w.H, w.d, w.causal)
     f_bwd = W.flops_backward(sl, w.H, w.d, w.causal)
     pairs = W.valid_pairs(sl, w.causal) * w.H
@@ -491,7 +509,7 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):
         kernels[name] = {"avg_ms": ms, "algorithmic_tflop": algo / 1e12,
                          "achieved_tflops": algo / (ms * 1e-3) / 1e12,
                          "frac_of_peak": algo / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    dom = max(kernels, key=lambda k_: kernels[k_]["avg_ms"])
+    dom = max(("fwd", "bwd"), key=lambda k_: kernels[k_]["avg_ms"])   # launches of the step
     res = {
         "metric": METRIC,
         "value": value,
