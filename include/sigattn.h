@@ -64,6 +64,11 @@ extern "C" {
 #define SIGATTN_MAX_BATCH 256      /* B above this returns SIGATTN_ERR_UNSUPPORTED */
 #define SIGATTN_MAX_LEN 65535      /* Lmax above this returns SIGATTN_ERR_UNSUPPORTED */
 #define SIGATTN_MAX_ROW_STRIDE (1 << 22)  /* stride_l above this (elements): UNSUPPORTED */
+/* Work items of one pass (128-row query or key tiles, summed over sequences and heads;
+ * packed batches: B * H * ceil(max rows / 128)) above this return
+ * SIGATTN_ERR_UNSUPPORTED: one launch holds at most 2^32 - 1 work-items of 256 threads,
+ * and sigattn_bwd puts two passes into one launch. */
+#define SIGATTN_MAX_ITEMS ((1 << 23) - 1)
 
 typedef enum {
   SIGATTN_OK = 0,

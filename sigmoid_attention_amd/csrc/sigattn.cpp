@@ -54,6 +54,8 @@ double scale_of(const sigattn_problem* p) {
   return p->scale != 0.0f ? (double)p->scale : 1.0 / std::sqrt((double)p->d);
 }
 
+int tile_rows_d(int d, int pass);
+
 sigattn_status validate_problem(const sigattn_problem* p) {
   if (!p) return SIGATTN_ERR_INVALID_ARG;
   if (p->struct_size != sizeof(sigattn_problem)) return SIGATTN_ERR_INVALID_ARG;
@@ -87,6 +89,12 @@ sigattn_status validate_problem(const sigattn_problem* p) {
   const int64_t es = elem_size(p);
   if (((p->stride_l * es) & 15) || ((p->stride_h * es) & 15) || ((p->stride_b * es) & 15))
     return SIGATTN_ERR_ALIGNMENT;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int tile = tile_rows_d(p->d, pass);
+    int64_t items = 0;
+    for (int b = 0; b < p->B; ++b) items += (int64_t)p->H * ((p->seqlens[b] + tile - 1) / tile);
+    if (items > SIGATTN_MAX_ITEMS) return SIGATTN_ERR_UNSUPPORTED;
+  }
   return SIGATTN_OK;
 }
 
@@ -287,7 +295,7 @@ sigattn_status validate_varlen(const sigattn_varlen* p) {
     const int64_t rows = pass == 2 ? p->max_seqlen_k : p->max_seqlen_q;
     const int tile = pass == 0 ? sa::fwd_tile_rows(p->d) : pass == 1 ? sa::dq_tile_rows(p->d)
                                                                     : sa::dkdv_tile_rows(p->d);
-    if ((int64_t)p->B * p->H * ((rows + tile - 1) / tile) > 0x7fffffffLL)
+    if ((int64_t)p->B * p->H * ((rows + tile - 1) / tile) > SIGATTN_MAX_ITEMS)
       return SIGATTN_ERR_UNSUPPORTED;
   }
   return SIGATTN_OK;

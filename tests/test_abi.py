@@ -108,6 +108,18 @@ def test_validation_gate_fields(lib):
     assert S.validate(p) == 1
 
 
+def test_work_item_cap(lib):
+    """A pass of more than SIGATTN_MAX_ITEMS 128-row tiles is refused before launch (the
+    one-call backward's grid holds two passes); the cap itself is accepted."""
+    cap = (1 << 23) - 1
+    # 256 sequences of 65535 rows = 512 tiles each: 131072 tiles per head
+    p, keep = S.make_problem(256, 64, 65535, 64, [65535] * 256)
+    assert S.validate(p) == 2            # 64 heads: 2^23 tiles, one too many
+    p, keep = S.make_problem(256, 63, 65535, 64, [65535] * 256)
+    assert S.validate(p) == 0            # 63 heads: below the cap
+    assert 63 * 131072 <= cap < 64 * 131072
+
+
 def test_entry_points_reject_before_launch(lib):
     """Argument errors are returned synchronously and nothing is launched; these calls
     pass fake device pointers, which would fault if anything were enqueued."""
@@ -326,6 +338,8 @@ def _varlen(**kw):
     (lambda p: setattr(p, "scale", -2.0), 1),
     (lambda p: (setattr(p, "gate", 1 << 24), setattr(p, "gate_tau", -1.0)), 1),
     (lambda p: (setattr(p, "B", 1 << 20), setattr(p, "H", 64), setattr(p, "max_seqlen_k", 1 << 20)), 2),
+    # B * H * ceil(max rows / 128) one past the work-item cap (2^23 - 1)
+    (lambda p: (setattr(p, "B", 1 << 16), setattr(p, "H", 128), setattr(p, "max_seqlen_q", 100)), 2),
     (lambda p: setattr(p, "struct_size", 8), 1),
 ])
 def test_varlen_validation_before_launch(lib, mutate, code):
