@@ -63,6 +63,9 @@ def parse():
                     help="the pages' kernel sweep: L = 512..16384 at B*L = 16384 tokens, d = 64 "
                          "(32 heads) and 128 (16 heads), 0 %% and 25 %% padding; forward and "
                          "backward TFLOPS, mean and 99 %% interval over 250 iterations")
+    ap.add_argument("--packed", action="store_true",
+                    help="run the workload's sequences packed (device cu_seqlens, no padding) "
+                         "through sigattn_fwd_varlen and sigattn_bwd_varlen")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="lower bound on the oracle time of the CPU baseline sample")
     return ap.parse_args()
@@ -369,6 +372,12 @@ def main():
     if args.pmc_pass:
         pmc_pass(S, w, t, gate, sl, out_dtype, args.fast_math)
         return
+    if args.packed:
+        res = measure_packed(S, W, w, data, stream, args.steps, args.warmup, out_dtype,
+                             args.fast_math)
+        res["mode"] = mode
+        print(json.dumps(res))
+        return
     res = measure(S, W, w, t, gate, sl, stream, args.steps, args.warmup, out_dtype,
                   args.fast_math)
     res["mode"] = mode
@@ -440,6 +449,91 @@ def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False):
     return {"sweep": "kernel sweep, B*L = 16384 tokens, bidirectional, bf16 inputs, float "
                      "outputs, " + ("single bf16 operands" if fast_math else "hi+lo operands"),
             "iters": iters, "rows": rows}
+
+
+def measure_packed(S, W, w, data, stream, steps, warmup, out_dtype, fast_math):
+    """The workload's valid rows packed back to back ([rows, H, d], device cu_seqlens),
+    one step = sigattn_fwd_varlen + sigattn_bwd_varlen; the same FLOP count as the padded
+    layout. The two backward passes are also timed alone."""
+    import torch
+    dev = torch.device("cuda:0")
+    sl = [int(x) for x in data["seqlens"]]
+
+    def pack(x):   # [B, H, L, d] -> [sum n, H, d]
+        return np.concatenate([x[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(sl)], axis=0)
+
+    t = {k: torch.from_numpy(np.ascontiguousarray(pack(data[k]))).to(torch.bfloat16).to(dev)
+         for k in ("q", "k", "v", "do")}
+    gate = None
+    if data["gate"] is not None:
+        gate = torch.from_numpy(np.concatenate([data["gate"][b, :n] for b, n in enumerate(sl)])).to(dev)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(sl)]).astype(np.int32), device=dev)
+    mx = max(sl)
+    kw = dict(causal=w.causal, gate=gate, tau=w.tau, sink=w.sink, out_dtype=out_dtype,
+              fast_math=fast_math)
+    o = torch.empty(t["q"].shape, dtype=out_dtype, device=dev)
+    dq, dk, dv = torch.empty_like(o), torch.empty_like(o), torch.empty_like(o)
+    args = (t["q"], t["k"], t["v"], t["do"], cu, cu, mx, mx)
+    calls = {"fwd": lambda: S.fwd_varlen(t["q"], t["k"], t["v"], cu, cu, mx, mx, out=o, **kw),
+             "bwd": lambda: S.bwd_varlen(*args, out=(dq, dk, dv), **kw)}
+    alone = {"bwd_dq": lambda: S.bwd_dq_varlen(*args, out=dq, **kw),
+             "bwd_dkdv": lambda: S.bwd_dkdv_varlen(*args, out=(dk, dv), **kw)}
+    for _ in range(warmup):
+        for fn in list(calls.values()) + list(alone.values()):
+            fn()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for e in evs:
+        for i, fn in enumerate(calls.values()):
+            e[i].record(stream)
+            fn()
+        e[2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    per = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+           for i, name in enumerate(calls)}
+    for name, fn in alone.items():
+        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for e0, e1 in pe:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        per[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pe]))
+    f_fwd = W.flops_forward(data["seqlens"], w.H, w.d, w.causal)
+    f_bwd = W.flops_backward(data["seqlens"], w.H, w.d, w.causal)
+    pairs = W.valid_pairs(data["seqlens"], w.causal) * w.H
+    kernels = {}
+    for name, ms in per.items():
+        algo = PASS_FLOPS_PER_PAIR[name] * w.d * pairs
+        kernels[name] = {"avg_ms": ms, "algorithmic_tflop": algo / 1e12,
+                         "achieved_tflops": algo / (ms * 1e-3) / 1e12,
+                         "frac_of_peak": algo / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    dom = max(("fwd", "bwd"), key=lambda k_: kernels[k_]["avg_ms"])
+    bwd_ms = per["bwd"]
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "layout": "packed rows, device cu_seqlens", "B": w.B,
+                   "H": w.H, "d": w.d, "rows": int(sum(sl)), "seqlens": sl, "causal": w.causal,
+                   "gated": w.gate is not None, "seed": w.seed,
+                   "step": "sigattn_fwd_varlen + sigattn_bwd_varlen"},
+        "fwd_tflops": f_fwd / (per["fwd"] * 1e-3) / 1e12,
+        "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
+        "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma",
+                     "kernel": {"fwd": "fwd_kernel",
+                                "bwd": "bwd_kernel" if w.d == 64 else "dkdv_kernel + dq_kernel"}[dom],
+                     "achieved": kernels[dom]["achieved_tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": kernels[dom]["frac_of_peak"], "traffic": None},
+        "kernels": kernels,
+    }
 
 
 def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):

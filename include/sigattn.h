@@ -201,7 +201,9 @@ typedef struct sigattn_varlen {
 /* The bounds in cu_seqlens_q/k are read by the kernels and are not checked on the host;
  * a sequence longer than max_seqlen_q (queries) or max_seqlen_k (keys) is computed only
  * up to that bound. Returns SIGATTN_ERR_UNSUPPORTED when B * H * ceil(max / 128)
- * exceeds 2^31 - 1 work items. */
+ * exceeds SIGATTN_MAX_ITEMS for a pass. sigattn_bwd_varlen computes dq, dk and dv as the
+ * two backward calls do, bitwise the same, from one launch at d = 64 (as sigattn_bwd);
+ * dq, dk and dv must be distinct and alias no input. */
 sigattn_status sigattn_fwd_varlen(const sigattn_varlen* p, const void* q, const void* k,
                                   const void* v, void* o, void* stream);
 sigattn_status sigattn_bwd_dq_varlen(const sigattn_varlen* p, const void* q, const void* k,
@@ -209,6 +211,9 @@ sigattn_status sigattn_bwd_dq_varlen(const sigattn_varlen* p, const void* q, con
 sigattn_status sigattn_bwd_dkdv_varlen(const sigattn_varlen* p, const void* q,
                                        const void* k, const void* v, const void* dout,
                                        void* dk, void* dv, void* stream);
+sigattn_status sigattn_bwd_varlen(const sigattn_varlen* p, const void* q, const void* k,
+                                  const void* v, const void* dout, void* dq, void* dk, void* dv,
+                                  void* stream);
 
 /* ------------------- KV cache with threshold eviction, single-query decode -------------------
  *

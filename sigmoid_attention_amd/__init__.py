@@ -10,8 +10,10 @@ raises, there is no fallback.
     o, row_mass = fwd_rowsum(q, k, v, seqlens, ...)
     dq = bwd_dq(q, k, v, do, seqlens, ...)
     dk, dv = bwd_dkdv(q, k, v, do, seqlens, ...)
+    dq, dk, dv = bwd(q, k, v, do, seqlens, ...)            # both backward kernels, one call
     dk, dv, dg_head, dg = bwd_dkdv_dg(q, k, v, do, seqlens, gate=g, ...)
     o = fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k)      # packed [rows, H, d] batches
+    dq, dk, dv = bwd_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k)
     cache = KVCache(B, H, d, cap, gated=True, tau=0.05)   # KV cache with eviction
     cache.build(k, v, seqlens, gate=g); cache.append(k1, v1, g1); o1 = cache.decode(q1, bias)
 
@@ -29,8 +31,8 @@ import os
 import numpy as np
 
 __all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd", "bwd_dkdv_dg", "fwd_varlen",
-           "bwd_dq_varlen", "bwd_dkdv_varlen", "VarlenDesc", "KVCache", "CacheDesc",
-           "validate", "plan", "library_path", "load",
+           "bwd_dq_varlen", "bwd_dkdv_varlen", "bwd_varlen", "VarlenDesc", "KVCache",
+           "CacheDesc", "validate", "plan", "library_path", "load",
            "Problem", "SigattnError", "STATUS", "VERSION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -130,7 +132,9 @@ def load():
     lib.sigattn_fwd_varlen.argtypes = [VD, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dq_varlen.argtypes = [VD, vp, vp, vp, vp, vp, vp]
     lib.sigattn_bwd_dkdv_varlen.argtypes = [VD, vp, vp, vp, vp, vp, vp, vp]
-    for f in (lib.sigattn_fwd_varlen, lib.sigattn_bwd_dq_varlen, lib.sigattn_bwd_dkdv_varlen):
+    lib.sigattn_bwd_varlen.argtypes = [VD, vp, vp, vp, vp, vp, vp, vp, vp]
+    for f in (lib.sigattn_fwd_varlen, lib.sigattn_bwd_dq_varlen, lib.sigattn_bwd_dkdv_varlen,
+              lib.sigattn_bwd_varlen):
         f.restype = ctypes.c_int
     C = ctypes.POINTER(CacheDesc)
     i64 = ctypes.c_int64
@@ -149,7 +153,7 @@ def load():
     lib.sigattn_status_string.restype = ctypes.c_char_p
     lib.sigattn_version.restype = ctypes.c_int
     for f in (lib.sigattn_validate, lib.sigattn_fwd, lib.sigattn_fwd_rowsum, lib.sigattn_bwd_dq,
-              lib.sigattn_bwd_dkdv, lib.sigattn_bwd_dkdv_dg):
+              lib.sigattn_bwd_dkdv, lib.sigattn_bwd, lib.sigattn_bwd_dkdv_dg):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -571,3 +575,21 @@ def bwd_dkdv_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k, *, causal=False, gate
                                        v.data_ptr(), do.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                        _stream(q)), "sigattn_bwd_dkdv_varlen")
     return dk, dv
+
+
+def bwd_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k, *, causal=False, gate=None, tau=0.0,
+               sink=4, eps=1e-8, scale=0.0, bias=None, out=None, out_dtype=None,
+               fast_math=False):
+    """(dQ, dK, dV) of packed sequences in one call: the values of bwd_dq_varlen and
+    bwd_dkdv_varlen, from one launch of both kernels at d = 64."""
+    lib = load()
+    p = _varlen_desc(q, k, (v, do), cu_q, cu_k, max_q, max_k, causal, gate, tau, sink, eps,
+                     scale, bias, out_dtype, fast_math)
+    if out is None:
+        dq, dk, dv = _new_like(q, out_dtype), _new_like(k, out_dtype), _new_like(k, out_dtype)
+    else:
+        dq, dk, dv = out
+    _check(lib.sigattn_bwd_varlen(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                  _stream(q)), "sigattn_bwd_varlen")
+    return dq, dk, dv

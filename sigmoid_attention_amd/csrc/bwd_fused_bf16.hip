@@ -1,6 +1,6 @@
-// Both backward kernels in one launch (d = 64): the work list is the dK/dV pass's items
-// followed by the dQ pass's items, each workgroup running the body of the pass its item
-// belongs to. The bodies, their arithmetic and their outputs are those of the separate
+// Both backward kernels in one launch (d = 64, padded or packed batches): the work list
+// is the dK/dV pass's items followed by the dQ pass's items, each workgroup running the
+// body of the pass its item belongs to. The bodies, their arithmetic and their outputs are those of the separate
 // dQ and dK/dV kernels ("Better Models, Faster Training: Sigmoid Attention for
 // single-cell Foundation Models", section 4: one kernel for dQ, one for dK/dV, no
 // atomics); only the dispatch is shared, so the workgroups of one pass fill the slots
@@ -10,41 +10,55 @@
 
 namespace sa {
 
-template <bool CAUSAL, bool GATED, bool SPLIT>
+// a: the dK/dV pass's plan (nitems dK/dV items); nq_items dQ items follow them, with
+// tiles_q query tiles per (sequence, head) in packed mode (VL).
+template <bool CAUSAL, bool GATED, bool SPLIT, bool VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_kernel(const KArgs a, void* dq) {
+void bwd_kernel(const KArgs a, void* dq, int nq_items, int tiles_q) {
   using TQ = DqTraits<64, 2, GATED>;
   using TK = DkvTraits<64, 2>;
   constexpr int kBytesQ = TQ::NSTAGE * TQ::STAGE, kBytesK = TK::NSTAGE * TK::STAGE;
   __shared__ __attribute__((aligned(1024))) char smem[kBytesQ > kBytesK ? kBytesQ : kBytesK];
-  // both passes list the same sequences with the same number of 128-row tiles each
-  const int g = remap_block(blockIdx.x, 2 * a.nitems, a.xcd_chunk);
+  const int g = remap_block(blockIdx.x, a.nitems + nq_items, a.xcd_chunk);
   if (g < a.nitems) {
-    const Item it = uniform_item(decode_item(a, g, 0));
-    dkdv_body<64, 2, CAUSAL, GATED, SPLIT, false, false>(a, it, smem, a.out0, a.out1);
+    const Item it = uniform_item(VL ? varlen_item(a, g, a.tiles_per_seq, 1) : decode_item(a, g, 0));
+    if (VL && !it.valid) return;
+    dkdv_body<64, 2, CAUSAL, GATED, SPLIT, false, VL>(a, it, smem, a.out0, a.out1);
   } else {
-    const Item it = uniform_item(decode_item(a, g - a.nitems, CAUSAL ? 1 : 0));
-    dq_body<64, 2, CAUSAL, GATED, SPLIT, false>(a, it, smem, dq);
+    const int gq = g - a.nitems;
+    const Item it = uniform_item(VL ? varlen_item(a, gq, tiles_q, 0)
+                                    : decode_item(a, gq, CAUSAL ? 1 : 0));
+    if (VL && !it.valid) return;
+    dq_body<64, 2, CAUSAL, GATED, SPLIT, VL>(a, it, smem, dq);
   }
 }
 
 template <bool C, bool G, bool SP>
-static hipError_t launch_one(const KArgs& a, void* dq, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_kernel<C, G, SP>), dim3(2 * a.nitems), dim3(256), 0, st, a, dq);
+static hipError_t launch_one(const KArgs& a, void* dq, int nq_items, int tiles_q, hipStream_t st) {
+  const dim3 grid(a.nitems + nq_items);
+  if (a.varlen)
+    hipLaunchKernelGGL((bwd_kernel<C, G, SP, true>), grid, dim3(256), 0, st, a, dq, nq_items, tiles_q);
+  else
+    hipLaunchKernelGGL((bwd_kernel<C, G, SP, false>), grid, dim3(256), 0, st, a, dq, nq_items, tiles_q);
   return hipGetLastError();
 }
 
-// a: the dK/dV pass's plan (out0 = dK, out1 = dV); requires d = 64 and equal tile rows
-// for both passes.
-hipError_t launch_bwd_bf16(const KArgs& a, void* dq, bool causal, bool gated, bool split,
-                           hipStream_t st) {
+// a: the dK/dV pass's plan (out0 = dK, out1 = dV) at d = 64; the dQ pass uses the same
+// 128-row tiles: in the padded layout its items mirror the dK/dV items (nq_items =
+// a.nitems), in packed mode there are nq_items = B * H * tiles_q of them.
+hipError_t launch_bwd_bf16(const KArgs& a, void* dq, int nq_items, int tiles_q, bool causal,
+                           bool gated, bool split, hipStream_t st) {
   static_assert(DqTraits<64, 2, false>::BM == DkvTraits<64, 2>::BK, "tile rows differ");
   if (causal) {
-    if (gated) return split ? launch_one<true, true, true>(a, dq, st) : launch_one<true, true, false>(a, dq, st);
-    return split ? launch_one<true, false, true>(a, dq, st) : launch_one<true, false, false>(a, dq, st);
+    if (gated) return split ? launch_one<true, true, true>(a, dq, nq_items, tiles_q, st)
+                            : launch_one<true, true, false>(a, dq, nq_items, tiles_q, st);
+    return split ? launch_one<true, false, true>(a, dq, nq_items, tiles_q, st)
+                 : launch_one<true, false, false>(a, dq, nq_items, tiles_q, st);
   }
-  if (gated) return split ? launch_one<false, true, true>(a, dq, st) : launch_one<false, true, false>(a, dq, st);
-  return split ? launch_one<false, false, true>(a, dq, st) : launch_one<false, false, false>(a, dq, st);
+  if (gated) return split ? launch_one<false, true, true>(a, dq, nq_items, tiles_q, st)
+                          : launch_one<false, true, false>(a, dq, nq_items, tiles_q, st);
+  return split ? launch_one<false, false, true>(a, dq, nq_items, tiles_q, st)
+               : launch_one<false, false, false>(a, dq, nq_items, tiles_q, st);
 }
 
 }  // namespace sa

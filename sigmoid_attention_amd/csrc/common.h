@@ -243,9 +243,10 @@ struct DirectTile {
 // The work item of this workgroup, with every field made explicitly wave-uniform (scalar
 // registers), so that the tensor base pointers derived from it stay in scalar registers.
 // Packed mode: the item's sequence bounds come from the device arrays cu_q / cu_k.
-__device__ __forceinline__ Item varlen_item(const KArgs& a, int g) {
+// Packed-mode item g of a pass with T tiles per (sequence, head), over key rows or query
+// rows.
+__device__ __forceinline__ Item varlen_item(const KArgs& a, int g, int T, int over_keys) {
   Item it;
-  const int T = a.tiles_per_seq;
   it.t = g % T;
   const int bh = g / T;
   it.h = bh % a.H;
@@ -254,7 +255,7 @@ __device__ __forceinline__ Item varlen_item(const KArgs& a, int g) {
   it.nq = a.cu_q[it.b + 1] - q0;
   it.nk = a.cu_k[it.b + 1] - k0;
   it.diag = it.nk - it.nq;
-  const int rows = a.tiles_over_keys ? it.nk : it.nq;
+  const int rows = over_keys ? it.nk : it.nq;
   it.valid = it.t * a.tile < rows ? 1 : 0;
   // -beta * log2(e); the default beta = -ln(nk) gives log2(nk)
   it.c2 = a.bias ? -a.bias[it.b] * 1.4426950408889634f
@@ -263,6 +264,10 @@ __device__ __forceinline__ Item varlen_item(const KArgs& a, int g) {
   it.koff = (int64_t)k0 * a.sl + (int64_t)it.h * a.sh;
   it.goff = k0;
   return it;
+}
+
+__device__ __forceinline__ Item varlen_item(const KArgs& a, int g) {
+  return varlen_item(a, g, a.tiles_per_seq, a.tiles_over_keys);
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t x) {

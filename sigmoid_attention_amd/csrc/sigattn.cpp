@@ -21,7 +21,8 @@ namespace sa {
 hipError_t launch_fwd_bf16(const KArgs& a, int d, bool causal, bool gated, bool split, hipStream_t st);
 hipError_t launch_dq_bf16(const KArgs& a, int d, bool causal, bool gated, bool split, hipStream_t st);
 hipError_t launch_dkdv_bf16(const KArgs& a, int d, bool causal, bool gated, bool split, hipStream_t st);
-hipError_t launch_bwd_bf16(const KArgs& a, void* dq, bool causal, bool gated, bool split, hipStream_t st);
+hipError_t launch_bwd_bf16(const KArgs& a, void* dq, int nq_items, int tiles_q, bool causal,
+                           bool gated, bool split, hipStream_t st);
 int fwd_tile_rows(int d);
 int dq_tile_rows(int d);
 int dkdv_tile_rows(int d);
@@ -301,9 +302,9 @@ sigattn_status validate_varlen(const sigattn_varlen* p) {
   return SIGATTN_OK;
 }
 
-sigattn_status run_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k,
-                          const void* v, const void* dout, void* o0, void* o1, void* stream) {
-  KArgs a;
+// The kernel arguments of a packed-batch pass.
+void plan_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k,
+                 const void* v, const void* dout, void* o0, void* o1, KArgs& a) {
   std::memset(&a, 0, sizeof(a));
   const int tile = tile_rows_d(p->d, pass);
   const int64_t rows = pass == 2 ? p->max_seqlen_k : p->max_seqlen_q;
@@ -312,7 +313,6 @@ sigattn_status run_varlen(const sigattn_varlen* p, int pass, const void* q, cons
   a.tiles_per_seq = (int32_t)((rows + tile - 1) / tile);
   a.tiles_over_keys = pass == 2 ? 1 : 0;
   a.nitems = (int32_t)((int64_t)p->B * p->H * a.tiles_per_seq);
-  if (a.nitems == 0) return SIGATTN_OK;
   a.cu_q = p->cu_seqlens_q;
   a.cu_k = p->cu_seqlens_k;
   a.bias = p->bias;
@@ -330,6 +330,13 @@ sigattn_status run_varlen(const sigattn_varlen* p, int pass, const void* q, cons
   a.gate_sink = p->gate_sink;
   a.out_f32 = p->out_dtype == SIGATTN_F32 ? 1 : 0;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1;
+}
+
+sigattn_status run_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k,
+                          const void* v, const void* dout, void* o0, void* o1, void* stream) {
+  KArgs a;
+  plan_varlen(p, pass, q, k, v, dout, o0, o1, a);
+  if (a.nitems == 0) return SIGATTN_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool causal = p->causal != 0, gated = p->gate != nullptr, split = p->fast_math == 0;
   hipError_t e;
@@ -464,8 +471,8 @@ sigattn_status sigattn_bwd(const sigattn_problem* p, const void* q, const void* 
   KArgs a;
   plan_pass(p, 2, &a);
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = dk; a.out1 = dv;
-  if (a.nitems > 0 &&
-      sa::launch_bwd_bf16(a, dq, p->causal != 0, p->gate != nullptr, p->fast_math == 0, st) != hipSuccess)
+  if (a.nitems > 0 && sa::launch_bwd_bf16(a, dq, a.nitems, 0, p->causal != 0, p->gate != nullptr,
+                                          p->fast_math == 0, st) != hipSuccess)
     return SIGATTN_ERR_HIP;
   if ((s = zero_fill(p, dk, dv, st)) != SIGATTN_OK) return s;
   return zero_fill(p, dq, nullptr, st);
@@ -518,6 +525,29 @@ sigattn_status sigattn_bwd_dkdv_varlen(const sigattn_varlen* p, const void* q,
   void* out[2] = {dk, dv};
   if ((s = check_tensors(in, 4, out, 2)) != SIGATTN_OK) return s;
   return run_varlen(p, 2, q, k, v, dout, dk, dv, stream);
+}
+
+sigattn_status sigattn_bwd_varlen(const sigattn_varlen* p, const void* q, const void* k,
+                                  const void* v, const void* dout, void* dq, void* dk, void* dv,
+                                  void* stream) {
+  sigattn_status s = validate_varlen(p);
+  if (s != SIGATTN_OK) return s;
+  const void* in[4] = {q, k, v, dout};
+  void* out[3] = {dq, dk, dv};
+  if ((s = check_tensors(in, 4, out, 3)) != SIGATTN_OK) return s;
+  if (p->d != 64) {
+    if ((s = run_varlen(p, 2, q, k, v, dout, dk, dv, stream)) != SIGATTN_OK) return s;
+    return run_varlen(p, 1, q, k, v, dout, dq, nullptr, stream);
+  }
+  KArgs a;
+  plan_varlen(p, 2, q, k, v, dout, dk, dv, a);
+  const int tile = tile_rows_d(p->d, 1);
+  const int tiles_q = (int)((p->max_seqlen_q + tile - 1) / tile);
+  const int nq_items = (int)((int64_t)p->B * p->H * tiles_q);
+  if (a.nitems + nq_items == 0) return SIGATTN_OK;
+  return sa::launch_bwd_bf16(a, dq, nq_items, tiles_q, p->causal != 0, p->gate != nullptr,
+                             p->fast_math == 0, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? SIGATTN_OK : SIGATTN_ERR_HIP;
 }
 
 sigattn_status sigattn_cache_build(const sigattn_cache* c, const sigattn_problem* p,

@@ -353,6 +353,8 @@ def test_varlen_validation_before_launch(lib, mutate, code):
     assert lib.sigattn_bwd_dq_varlen(ctypes.byref(p), t[0], t[1], t[2], t[3], t[4], None) == code
     assert lib.sigattn_bwd_dkdv_varlen(ctypes.byref(p), t[0], t[1], t[2], t[3], t[4], t[5],
                                        None) == code
+    assert lib.sigattn_bwd_varlen(ctypes.byref(p), t[0], t[1], t[2], t[3], t[4], t[5],
+                                  vp(1 << 24), None) == code
 
 
 def test_varlen_output_checks(lib):
@@ -364,3 +366,9 @@ def test_varlen_output_checks(lib):
     assert lib.sigattn_fwd_varlen(ctypes.byref(p), vp((1 << 21) + 4), k, v, vp(1 << 24), None) == 3
     two = vp(1 << 25)
     assert lib.sigattn_bwd_dkdv_varlen(ctypes.byref(p), q, k, v, q, two, two, None) == 1
+    three, four = vp(1 << 26), vp(1 << 27)
+    assert lib.sigattn_bwd_varlen(ctypes.byref(p), q, k, v, q, two, two, three, None) == 1
+    assert lib.sigattn_bwd_varlen(ctypes.byref(p), q, k, v, q, two, three, k, None) == 1
+    assert lib.sigattn_bwd_varlen(ctypes.byref(p), q, k, v, q, None, three, four, None) == 1
+    assert lib.sigattn_bwd_varlen(ctypes.byref(p), q, k, v, q, vp((1 << 25) + 8), three, four,
+                                  None) == 3

@@ -157,3 +157,68 @@ def test_varlen_length_grid(d, causal):
     note(f"varlen length grid d={d} causal={causal}")
     gpu = _run(torch, c, causal)
     print(_check(gpu, c, causal, label=f"grid {d} {causal}"))
+
+
+def _one_call(torch, c, causal, tau=0.0, out_dtype=None, fast=False):
+    dev = torch.device("cuda")
+    t = {n: torch.from_numpy(c[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do")}
+    cu_q = torch.from_numpy(c["cu_q"]).to(dev)
+    cu_k = torch.from_numpy(c["cu_k"]).to(dev)
+    gate = None if c["gate"] is None else torch.from_numpy(c["gate"]).to(dev)
+    kw = dict(causal=causal, gate=gate, tau=tau, sink=4, out_dtype=out_dtype or torch.float32,
+              fast_math=fast)
+    args = (t["q"], t["k"], t["v"], t["do"], cu_q, cu_k, c["max_q"], c["max_k"])
+    od = kw["out_dtype"]
+
+    def filled(like):   # rows outside the sequences must stay as they are
+        return torch.full(like.shape, SENTINEL, dtype=od, device=dev)
+
+    one = S.bwd_varlen(*args, out=(filled(t["q"]), filled(t["k"]), filled(t["k"])), **kw)
+    dq = S.bwd_dq_varlen(*args, out=filled(t["q"]), **kw)
+    dk, dv = S.bwd_dkdv_varlen(*args, out=(filled(t["k"]), filled(t["k"])), **kw)
+    torch.cuda.synchronize()
+    return one, (dq, dk, dv)
+
+
+@pytest.mark.parametrize("fast", [False, True])
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("d", [64, 128])
+def test_one_call_backward_bitwise(d, case, causal, gated, fast):
+    """sigattn_bwd_varlen equals sigattn_bwd_dq_varlen + sigattn_bwd_dkdv_varlen bitwise
+    (the same kernel bodies; one launch at d = 64), including unequal query and key
+    lengths, so the two lists of items differ in length."""
+    torch = need_gpu()
+    lq, lk = CASES[case]
+    c = _packed_case(450 + d + len(case) + 2 * causal + gated, lq, lk, 3, d, gated=gated)
+    note(f"varlen one-call backward d={d} {case} causal={causal} gated={gated} fast={fast}")
+    for od in (torch.float32, torch.bfloat16):
+        one, sep = _one_call(torch, c, causal, tau=0.05 if gated else 0.0, out_dtype=od, fast=fast)
+        for name, a, b in zip(("dQ", "dK", "dV"), one, sep):
+            ia = a.view(torch.int16 if a.element_size() == 2 else torch.int32)
+            ib = b.view(torch.int16 if b.element_size() == 2 else torch.int32)
+            assert torch.equal(ia, ib), f"{case} d={d} {name}: one-call differs"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_call_backward_against_oracle(causal):
+    """The packed one-call backward at the stated bar, on the length grid (196 sequences,
+    more queries than keys and the reverse) and the unequal case."""
+    torch = need_gpu()
+    grid = [1, 31, 32, 33, 63, 64, 65, 95, 96, 127, 128, 129, 160, 200]
+    lq = [a for a in grid for _ in grid]
+    lk = [b for _ in grid for b in grid]
+    c = _packed_case(470 + causal, lq, lk, 1, 64, gated=True)
+    note(f"varlen one-call backward vs oracle causal={causal}")
+    one, _ = _one_call(torch, c, causal, tau=0.05)
+    rows_q, rows_k = int(c["cu_q"][-1]), int(c["cu_k"][-1])
+    for g, rows in zip(one, (rows_q, rows_k, rows_k)):
+        assert bool((g[rows:] == SENTINEL).all()), "rows outside the sequences written"
+    kw = dict(causal=causal, gate=c["gate"], tau=0.05, sink=4)
+    ref = O.backward_varlen(c["q"], c["k"], c["v"], c["do"], c["cu_q"], c["cu_k"], **kw)
+    for name, g, r, rows in zip(("dQ", "dK", "dV"), one, ref, (rows_q, rows_k, rows_k)):
+        g = g.cpu().numpy()[:rows]
+        e = err_ratio(g, r[:rows], np.ones(g.shape, bool))
+        assert e <= BF16_TOL, f"{name}: {e:.3e}"
+
