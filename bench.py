@@ -66,52 +66,62 @@ def parse():
     ap.add_argument("--packed", action="store_true",
                     help="run the workload's sequences packed (device cu_seqlens, no padding) "
                          "through sigattn_fwd_varlen and sigattn_bwd_varlen")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="lower bound on the oracle time of the CPU baseline sample")
     return ap.parse_args()
 
 
 def cpu_baseline(data, w, min_seconds):
     """Time the oracle, as it stands, on a bounded sample of the same workload: full
-    forward + backward of whole heads of the batch entry with the median length, one
-    head after another until at least `min_seconds` have passed (or all heads of that
-    entry are done), on the host cores."""
+    forward + backward of whole (batch entry, head) pairs, starting with the entry of
+    median length and going on to the entries closest to it, one head after another
+    until at least `min_seconds` have passed (or the workload is done), on the host
+    cores."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    sl = data["seqlens"]
-    b = int(np.argsort(sl)[len(sl) // 2])
-    n = int(sl[b])
+    sl = [int(x) for x in data["seqlens"]]
+    med = sorted(sl)[len(sl) // 2]
+    order = sorted((b for b in range(len(sl)) if sl[b] > 0), key=lambda b: (abs(sl[b] - med), b))
     kw = dict(causal=w.causal)
     t_fwd = t_bwd = 0.0
-    heads = 0
-    for h in range(w.H):
-        q = data["q"][b:b + 1, h:h + 1].astype(np.float64)
-        k = data["k"][b:b + 1, h:h + 1].astype(np.float64)
-        v = data["v"][b:b + 1, h:h + 1].astype(np.float64)
-        do = data["do"][b:b + 1, h:h + 1].astype(np.float64)
-        t0 = time.perf_counter()
-        oracle.forward(q, k, v, [n], **kw)
-        t1 = time.perf_counter()
-        oracle.backward(q, k, v, do, [n], **kw)
-        t2 = time.perf_counter()
-        t_fwd += t1 - t0
-        t_bwd += t2 - t1
-        heads += 1
+    pairs = 0
+    done = []   # (batch entry, heads done)
+    for b in order:
+        n = sl[b]
+        for h in range(w.H):
+            q = data["q"][b:b + 1, h:h + 1].astype(np.float64)
+            k = data["k"][b:b + 1, h:h + 1].astype(np.float64)
+            v = data["v"][b:b + 1, h:h + 1].astype(np.float64)
+            do = data["do"][b:b + 1, h:h + 1].astype(np.float64)
+            t0 = time.perf_counter()
+            oracle.forward(q, k, v, [n], **kw)
+            t1 = time.perf_counter()
+            oracle.backward(q, k, v, do, [n], **kw)
+            t2 = time.perf_counter()
+            t_fwd += t1 - t0
+            t_bwd += t2 - t1
+            pairs += n * (n + 1) // 2 if w.causal else n * n
+            if done and done[-1][0] == b:
+                done[-1] = (b, done[-1][1] + 1)
+            else:
+                done.append((b, 1))
+            if t_fwd + t_bwd >= min_seconds:
+                break
         if t_fwd + t_bwd >= min_seconds:
             break
-    pairs = (n * (n + 1) // 2 if w.causal else n * n) * heads
     flops = 4.0 * w.d * pairs * 3.5   # forward + credited backward (2.5x forward)
+    parts = ", ".join(f"{hd} of {w.H} heads of entry {b} (n={sl[b]})" for b, hd in done)
     return {
         "value": flops / (t_fwd + t_bwd) / 1e12,
         "unit": "TFLOPS",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle, forward+backward of {heads} of the {w.H} heads of "
-                  f"batch entry {b} (n={n}) of {w.name}; fwd {t_fwd:.2f} s, bwd {t_bwd:.2f} s",
+        "sample": f"fp64 numpy oracle, forward+backward of {parts} of {w.name}; "
+                  f"fwd {t_fwd:.2f} s, bwd {t_bwd:.2f} s",
         "host": platform.processor() or platform.machine(),
         "host_cpus": os.cpu_count(),
     }
