@@ -32,6 +32,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 #define SA_LDS __attribute__((address_space(3)))
 
@@ -42,6 +43,10 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -315,6 +320,24 @@ __device__ __forceinline__ void wait_vmem_and_barrier() {
 __device__ __forceinline__ float sigmoid_l2(float acc, float c1, float c2) {
   const float t = __builtin_fmaf(acc, c1, c2);
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+}
+
+// 8 floats to f16, round to nearest even.
+__device__ __forceinline__ f16x8 pack8_f16(const f32x16& v, int base) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (_Float16)v[base + i];
+  return r;
+}
+
+// Logistic function scaled by 2^14: 2^14 / (1 + 2^t) = 1 / (2^-14 + 2^(t - 14)), with
+// c2s = c2 - 14 folded into the exp2 argument, so the scale costs nothing. In [0, 2^14],
+// so the value and its f16 rounding stay normal down to sigma = 2^-28.
+constexpr float kPScale = 16384.0f;
+constexpr float kPScaleInv = 1.0f / 16384.0f;
+__device__ __forceinline__ float sigmoid_l2s(float acc, float c1, float c2s) {
+  const float t = __builtin_fmaf(acc, c1, c2s);
+  return __builtin_amdgcn_rcpf(kPScaleInv + __builtin_amdgcn_exp2f(t));
 }
 
 __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {

@@ -67,6 +67,8 @@ void fwd_kernel(const KArgs a) {
   using T = FwdTraits<D, QB, CPT, GATED>;
   using Tile = DirectTile<T::BN, D, T::kWaves>;
   __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
+  // SPLIT: per ring slot, set when some value of that tile's V does not fit f16
+  __shared__ int vflag[T::NSTAGE];
 
   const int l = lane_id(), w = wave_id();
   const int lk = 4 * (l >> 5);
@@ -86,6 +88,7 @@ void fwd_kernel(const KArgs a) {
   const int item_q0 = it.t * T::BM;
   const int q0 = item_q0 + w * QB * 32;   // first query of this wave
   const float c1 = a.c1, c2 = it.c2;
+  const float c2s = c2 - 14.0f;   // exp2 argument of the 2^14-scaled logistic function
 
   // keys of the item: all of them, or (causal) those up to the item's last query + diag
   int kend = nk;
@@ -116,10 +119,52 @@ void fwd_kernel(const KArgs a) {
       const int key = t * T::BN + l;
       const float g = Gg[key < lastk ? key : lastk];
       const bool keep = key < nk && !(key >= a.gate_sink && g < a.gate_tau);
-      tab[l] = keep ? c2 - __builtin_amdgcn_logf(g + a.gate_eps) : __builtin_inff();
+      tab[l] = keep ? c2s - __builtin_amdgcn_logf(g + a.gate_eps) : __builtin_inff();
       tab[T::BN + l] = keep ? g : 0.0f;
     }
   };
+  // SPLIT: P V runs on f16 operands where V allows. P is kept as 2^14 sigma (in [0, 2^14],
+  // normal in f16 down to sigma = 2^-28) and rounded once to f16, 2^-11 relative, 8x
+  // finer than bf16: one f16 product instead of the bf16 hi + lo pair. V's bf16 values
+  // are exact in f16 below 2^16 in magnitude; during tile t each thread converts its two
+  // 16-byte chunks of tile t+1's V in place if all 16 values fit, and otherwise leaves
+  // them and flags the tile. If any tile of the item was flagged, the workgroup computes
+  // the item again from the start on bf16 hi + lo operands (V unconverted). The tile
+  // loops themselves never branch on the flags: an exit from them costs the register
+  // allocation far more than the rare second pass.
+  static_assert(T::TILE == 16 * 2 * T::kThreads, "two 16-byte V chunks per thread");
+  auto convert_v = [&](int t) -> bool {
+    char* vt = smem + (t % T::NSTAGE) * T::STAGE + T::TILE;
+    u32x4 c[2];
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      c[i] = *reinterpret_cast<const u32x4*>(vt + 16 * (threadIdx.x + T::kThreads * i));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __builtin_bit_cast(float, c[i][e] << 16);
+        const float hi = __builtin_bit_cast(float, c[i][e] & 0xffff0000u);
+        bad |= !(__builtin_fabsf(lo) < 65536.0f) || !(__builtin_fabsf(hi) < 65536.0f);
+      }
+    }
+    if (!bad) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const _Float16 lo = (_Float16)__builtin_bit_cast(float, c[i][e] << 16);
+          const _Float16 hi = (_Float16)__builtin_bit_cast(float, c[i][e] & 0xffff0000u);
+          o[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        *reinterpret_cast<u32x4*>(vt + 16 * (threadIdx.x + T::kThreads * i)) = o;
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && l == 0) vflag[t % T::NSTAGE] = 1;
+    return !bad;
+  };
+  if (SPLIT && threadIdx.x < T::NSTAGE) vflag[threadIdx.x] = 0;
   if (ntiles > 0) {
     issue_tile(0);
     fill_table(0);
@@ -160,6 +205,11 @@ void fwd_kernel(const KArgs a) {
     for (int ks = 0; ks < T::KS; ++ks)
       s_cur = mfma(lds_row_operand<D>(smem, 0, 16 * ks), qop[0][ks], s_cur);
   }
+  int vbad = 0;   // SPLIT: some tile of this item had V beyond f16
+  if (SPLIT && ntiles > 0) {
+    convert_v(0);
+    __syncthreads();
+  }
 
   // The work of a chunk is split into units u = (chunk c, query block qb). Unit u
   // evaluates the logistic function of S(u) while the MFMAs of S(u+1) run, then adds
@@ -187,7 +237,7 @@ void fwd_kernel(const KArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = r0 + e;
-      float x = sigmoid_l2(s_cur[r], c1, GATED ? tc2[e] : c2);
+      float x = sigmoid_l2s(s_cur[r], c1, GATED ? tc2[e] : c2s);
       if (MODE == kMasked) x = arc(r) <= lim ? x : 0.0f;
       if (RS) part += x;
       if (GATED) x *= tg[e];
@@ -217,8 +267,9 @@ void fwd_kernel(const KArgs a) {
   //   4: entries 12-15, to bf16 (h = 1)    | -
   //   5: -                                 | P V (h = 1)
   const LdsLane<D> lane;
-  auto unit = [&](auto mode_tag, int qb, const char* Kn, int kn_row, int qb_next,
-                         const char* Vt, int v_row, const float* tab, int kb) {
+  auto unit = [&](auto mode_tag, auto f16_tag, int qb, const char* Kn, int kn_row,
+                  int qb_next, const char* Vt, int v_row, const float* tab, int kb) {
+    constexpr bool F16 = decltype(f16_tag)::value;
     bf16x8 kop[T::KS];
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lane.rowop(Kn, kn_row, ks);
@@ -228,13 +279,15 @@ void fwd_kernel(const KArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     f32x16 p;
     bf16x8 ph0, pl0, ph1, pl1;
+    f16x8 p16_0, p16_1;
     f32x16 s_next = zero16();
     sig4(mode_tag, qb, 0, kb, tab, v_row, p);
 #pragma unroll
     for (int ks = 0; ks < T::KS / 2; ++ks) s_next = mfma(kop[ks], qop[qb_next][ks], s_next);
     __builtin_amdgcn_sched_barrier(0);
     sig4(mode_tag, qb, 4, kb, tab, v_row, p);
-    to_bf16(p, 0, ph0, pl0);
+    if constexpr (F16) p16_0 = pack8_f16(p, 0);
+    else to_bf16(p, 0, ph0, pl0);
 #pragma unroll
     for (int ks = T::KS / 2; ks < T::KS; ++ks) s_next = mfma(kop[ks], qop[qb_next][ks], s_next);
     __builtin_amdgcn_sched_barrier(0);
@@ -243,24 +296,31 @@ void fwd_kernel(const KArgs a) {
     for (int dt = 0; dt < T::DT; ++dt) vop1[dt] = lane.colop(Vt, v_row + 16, dt);
     sig4(mode_tag, qb, 8, kb, tab, v_row, p);
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) pv(qb, dt, vop0[dt], ph0, pl0);
+    for (int dt = 0; dt < T::DT; ++dt) {
+      if constexpr (F16) acc[qb][dt] = mfma_f16(__builtin_bit_cast(f16x8, vop0[dt]), p16_0, acc[qb][dt]);
+      else pv(qb, dt, vop0[dt], ph0, pl0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     sig4(mode_tag, qb, 12, kb, tab, v_row, p);
-    to_bf16(p, 1, ph1, pl1);
+    if constexpr (F16) p16_1 = pack8_f16(p, 8);
+    else to_bf16(p, 1, ph1, pl1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) pv(qb, dt, vop1[dt], ph1, pl1);
+    for (int dt = 0; dt < T::DT; ++dt) {
+      if constexpr (F16) acc[qb][dt] = mfma_f16(__builtin_bit_cast(f16x8, vop1[dt]), p16_1, acc[qb][dt]);
+      else pv(qb, dt, vop1[dt], ph1, pl1);
+    }
     __builtin_amdgcn_sched_barrier(0);
     s_cur = s_next;
   };
-  auto chunk = [&](auto mode_tag, const char* Kc, int kc_row, const char* Kn, int kn_row,
-                   const char* Vt, int v_row, const float* tab, int kb) {
+  auto chunk = [&](auto mode_tag, auto f16_tag, const char* Kc, int kc_row, const char* Kn,
+                   int kn_row, const char* Vt, int v_row, const float* tab, int kb) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const char* K1 = qb + 1 < QB ? Kc : Kn;
       const int k1_row = qb + 1 < QB ? kc_row : kn_row;
       const int qb1 = qb + 1 < QB ? qb + 1 : 0;
-      unit(mode_tag, qb, K1, k1_row, qb1, Vt, v_row, tab, kb);
+      unit(mode_tag, f16_tag, qb, K1, k1_row, qb1, Vt, v_row, tab, kb);
     }
   };
 
@@ -280,14 +340,22 @@ void fwd_kernel(const KArgs a) {
   // One tile. `stage` is the ring slot of tile t: a compile-time constant in the unrolled
   // interior loop (the LDS addresses then fold into immediate offsets), or -1 when it
   // has to be computed.
-  auto tile_body = [&](auto mode_tag, auto stage_tag, int t) {
+  auto tile_body = [&](auto mode_tag, auto stage_tag, auto f16_tag, int t) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr int SG = decltype(stage_tag)::value;
+    constexpr bool F16 = decltype(f16_tag)::value;
     if (t > 0) wait_vmem_and_barrier();
-    if (t + 2 < ntiles) issue_tile(t + 2);
-    if (t + 1 < ntiles) fill_table(t + 1);
     const int st = SG >= 0 ? SG : t % T::NSTAGE;
     const int st1 = SG >= 0 ? (SG + 1) % T::NSTAGE : (t + 1) % T::NSTAGE;
+    // every thread reads the flag after the barrier that follows all its writers
+    if constexpr (F16) vbad |= vflag[st];
+    if (t + 2 < ntiles) issue_tile(t + 2);
+    if (t + 1 < ntiles) fill_table(t + 1);
+    if constexpr (F16) {
+      // tile t+2's slot was last read at the start of tile t-1
+      if (threadIdx.x == 0) vflag[(st + 2) % T::NSTAGE] = 0;
+      if (t + 1 < ntiles) convert_v(t + 1);
+    }
     const char* cur = smem + st * T::STAGE;
     const char* nxt = smem + st1 * T::STAGE;
     const float* tab = reinterpret_cast<const float*>(cur + 2 * T::TILE);
@@ -297,21 +365,53 @@ void fwd_kernel(const KArgs a) {
       if (MODE == kInterior || c < wch) {
         const char* Kn = (cc + 1 < CPT) ? cur : nxt;
         const int kn_row = ((cc + 1) % CPT) * 32;
-        chunk(mode_tag, cur, cc * 32, Kn, kn_row, cur + T::TILE, cc * 32, tab, c * 32);
+        chunk(mode_tag, f16_tag, cur, cc * 32, Kn, kn_row, cur + T::TILE, cc * 32, tab, c * 32);
       }
     }
   };
   using Int = std::integral_constant<int, kInterior>;
   using Msk = std::integral_constant<int, kMasked>;
   using Dyn = std::integral_constant<int, -1>;
-  int t = 0;
-  for (; t + 3 <= tmask; t += 3) {
-    tile_body(Int{}, std::integral_constant<int, 0>{}, t);
-    tile_body(Int{}, std::integral_constant<int, 1>{}, t + 1);
-    tile_body(Int{}, std::integral_constant<int, 2>{}, t + 2);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using Op16 = std::true_type;     // f16 operands
+  using OpBf = std::false_type;    // bf16 operands (hi + lo when SPLIT)
+  auto tile_loops = [&](auto f16_tag) {
+    int t = 0;
+    for (; t + 3 <= tmask; t += 3) {
+      tile_body(Int{}, S0{}, f16_tag, t);
+      tile_body(Int{}, S1{}, f16_tag, t + 1);
+      tile_body(Int{}, S2{}, f16_tag, t + 2);
+    }
+    for (; t < tmask; ++t) tile_body(Int{}, Dyn{}, f16_tag, t);
+    for (; t < ntiles; ++t) tile_body(Msk{}, Dyn{}, f16_tag, t);
+  };
+  if constexpr (SPLIT) {
+    tile_loops(Op16{});
+    if (__builtin_amdgcn_readfirstlane(vbad)) {
+      // again from the start on bf16 hi + lo operands: wait for the loads still in flight
+      // and for every wave to leave the ring, then refill it
+      wait_vmem_and_barrier();
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        mass[qb] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) acc[qb][dt] = zero16();
+      }
+      issue_tile(0);
+      fill_table(0);
+      if (ntiles > 1) issue_tile(1);
+      wait_vmem_and_barrier();
+      s_cur = zero16();
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks)
+        s_cur = mfma(lds_row_operand<D>(smem, 0, 16 * ks), qop[0][ks], s_cur);
+      tile_loops(OpBf{});
+    }
+  } else {
+    tile_loops(OpBf{});
   }
-  for (; t < tmask; ++t) tile_body(Int{}, Dyn{}, t);
-  for (; t < ntiles; ++t) tile_body(Msk{}, Dyn{}, t);
 
   // epilogue: valid query rows only (rows >= n are zero-filled by a separate kernel)
   if (RS) {
@@ -319,7 +419,8 @@ void fwd_kernel(const KArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
       mass[qb] += __shfl_xor(mass[qb], 32, 64);
       const int query = q0 + 32 * qb + (l & 31);
-      if (l < 32 && query < nq) a.aux[((int64_t)it.b * a.H + it.h) * a.Lmax + query] = mass[qb];
+      if (l < 32 && query < nq)
+        a.aux[((int64_t)it.b * a.H + it.h) * a.Lmax + query] = mass[qb] * kPScaleInv;
     }
   }
 #pragma unroll
@@ -328,7 +429,8 @@ void fwd_kernel(const KArgs a) {
     if (query < nq) {
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
-        store_row(a.out0, it.qoff + (int64_t)query * sl, a.out_f32, acc[qb][dt], 32 * dt, 1.0f);
+        store_row(a.out0, it.qoff + (int64_t)query * sl, a.out_f32, acc[qb][dt], 32 * dt,
+                  kPScaleInv);
     }
   }
 }

@@ -12,8 +12,10 @@ Two checks are used.
     bf16 output rounding        |d| <= u |ref|
     fast math (P or dS in bf16) |d| <= u A,  A = sum of |terms| of the product
                                 (the oracle's absolute sums)
-  plus 2^-12 A for the hi + lo residual and float accumulation, and 2e-3 rms(ref) for
-  the float evaluation of sigma near saturation (|delta sigma'| <= 2^-23).
+  plus 2^-12 A for the hi + lo residual and float accumulation (2^-11 A for the forward
+  output in the default mode, whose P V product takes P rounded once to f16, unit
+  roundoff 2^-11), and 2e-3 rms(ref) for the float evaluation of sigma near saturation
+  (|delta sigma'| <= 2^-23).
 """
 
 import sys
@@ -126,9 +128,10 @@ def check_all(gpu, ref, seqlens, tol, label=""):
     return report
 
 
-def bound_excess(gpu, ref, mag, bf16_out, fast_math, rms):
-    """max over elements of |gpu - ref| / (derived bound); <= 1 passes."""
-    bound = (2.0 ** -12) * mag + 2e-3 * rms
+def bound_excess(gpu, ref, mag, bf16_out, fast_math, rms, f16_p=False):
+    """max over elements of |gpu - ref| / (derived bound); <= 1 passes. f16_p: the output
+    of a product whose P operand is rounded to f16 in the default mode (the forward)."""
+    bound = (2.0 ** (-11 if f16_p and not fast_math else -12)) * mag + 2e-3 * rms
     if fast_math:
         bound = bound + U_BF16 * mag
     if bf16_out:
@@ -146,7 +149,7 @@ def check_bounds(gpu, ref, mag, seqlens, bf16_out, fast_math, label=""):
         assert np.all(np.isfinite(g)), f"{label} {name}: non-finite values"
         assert np.all(gpu[name][~mask] == 0.0), f"{label} {name}: padded rows not exactly 0"
         rms = float(np.sqrt(np.mean(r * r)))
-        x = bound_excess(g, r, m, bf16_out, fast_math, rms)
+        x = bound_excess(g, r, m, bf16_out, fast_math, rms, f16_p=name == "O")
         report[name] = x
         assert x <= 1.0, f"{label} {name}: error exceeds the derived bound by {x:.2f}x"
     return report

@@ -176,3 +176,25 @@ def test_full_size_sampled(name):
         for key in ("O", "dQ", "dK", "dV"):
             assert np.all(np.isfinite(out[key][mask]))
             assert np.all(out[key][~mask] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_values_beyond_f16(d, causal):
+    """V values beyond the f16 range (|v| >= 2^16) in some tiles: those items run again
+    on bf16 hi + lo operands; everything still meets the stated bar, padded rows 0."""
+    torch = need_gpu()
+    w = W.Workload(f"big_v_{d}", "bf16", 3, 2, d, 600, ("fixed", [600, 333, 65]),
+                   seed=700 + d + causal, causal=causal)
+    data = W.generate(w)
+    v = data["v"]
+    v[0, 1, 100:104] *= 3e5                      # one tile of one head
+    v[2, 0, 64] = W.round_to_bf16(np.full(d, -7.0e4, np.float32))
+    v[1, 0, 5, 3] = np.float32(65280.0)           # the largest bf16 below 2^16 stays f16
+    data["v"] = W.round_to_bf16(v)
+    ref, mag = oracle_full(data), oracle_magnitudes(data)
+    note(f"V beyond f16 d={d} causal={causal}")
+    gpu = run_gpu(data, torch.bfloat16, out_dtype=torch.float32)
+    print(check_all(gpu, ref, data["seqlens"], BF16_TOL, f"big V {d}"))
+    print(check_bounds(gpu, ref, mag, data["seqlens"], False, False, f"big V {d}"))
+
