@@ -127,42 +127,36 @@ void fwd_kernel(const KArgs a) {
   // normal in f16 down to sigma = 2^-28) and rounded once to f16, 2^-11 relative, 8x
   // finer than bf16: one f16 product instead of the bf16 hi + lo pair. V's bf16 values
   // are exact in f16 below 2^16 in magnitude; during tile t each thread converts its two
-  // 16-byte chunks of tile t+1's V in place if all 16 values fit, and otherwise leaves
-  // them and flags the tile. If any tile of the item was flagged, the workgroup computes
-  // the item again from the start on bf16 hi + lo operands (V unconverted). The tile
+  // 16-byte chunks of tile t+1's V in place and flags the tile if a value did not fit.
+  // If any tile of the item was flagged, the workgroup computes the item again from the
+  // start on bf16 hi + lo operands, with V loaded afresh and left unconverted. The tile
   // loops themselves never branch on the flags: an exit from them costs the register
   // allocation far more than the rare second pass.
   static_assert(T::TILE == 16 * 2 * T::kThreads, "two 16-byte V chunks per thread");
-  auto convert_v = [&](int t) -> bool {
+  auto convert_v = [&](int t) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     char* vt = smem + (t % T::NSTAGE) * T::STAGE + T::TILE;
-    u32x4 c[2];
-    bool bad = false;
+    u16x2 emax = {0, 0};   // largest |bf16| bit pattern seen, per half
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      c[i] = *reinterpret_cast<const u32x4*>(vt + 16 * (threadIdx.x + T::kThreads * i));
+      u32x4* p = reinterpret_cast<u32x4*>(vt + 16 * (threadIdx.x + T::kThreads * i));
+      const u32x4 c = *p;
+      u32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = __builtin_bit_cast(float, c[i][e] << 16);
-        const float hi = __builtin_bit_cast(float, c[i][e] & 0xffff0000u);
-        bad |= !(__builtin_fabsf(lo) < 65536.0f) || !(__builtin_fabsf(hi) < 65536.0f);
+        emax = __builtin_elementwise_max(emax, __builtin_bit_cast(u16x2, c[e] & 0x7fff7fffu));
+        f16x2 h;
+        h[0] = (_Float16)__builtin_bit_cast(float, c[e] << 16);
+        h[1] = (_Float16)__builtin_bit_cast(float, c[e] & 0xffff0000u);
+        o[e] = __builtin_bit_cast(uint32_t, h);
       }
+      *p = o;
     }
-    if (!bad) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const _Float16 lo = (_Float16)__builtin_bit_cast(float, c[i][e] << 16);
-          const _Float16 hi = (_Float16)__builtin_bit_cast(float, c[i][e] & 0xffff0000u);
-          o[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-        *reinterpret_cast<u32x4*>(vt + 16 * (threadIdx.x + T::kThreads * i)) = o;
-      }
-    }
+    // |v| >= 2^16 is a bf16 exponent field >= 143 (0x4780 with the mantissa bits below);
+    // that includes infinities, and NaN, which would not need the second pass but is rare
+    const bool bad = emax[0] >= 0x4780 || emax[1] >= 0x4780;
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && l == 0) vflag[t % T::NSTAGE] = 1;
-    return !bad;
   };
   if (SPLIT && threadIdx.x < T::NSTAGE) vflag[threadIdx.x] = 0;
   if (ntiles > 0) {
