@@ -222,3 +222,14 @@ def test_one_call_backward_against_oracle(causal):
         e = err_ratio(g, r[:rows], np.ones(g.shape, bool))
         assert e <= BF16_TOL, f"{name}: {e:.3e}"
 
+
+def test_varlen_values_beyond_f16():
+    """Packed batches whose V exceeds the f16 range in one sequence: the forward's second
+    pass on bf16 operands covers packed items too."""
+    torch = need_gpu()
+    c = _packed_case(480, [300, 129, 64], [300, 129, 64], 2, 64)
+    c["v"][310:314] = W.round_to_bf16(c["v"][310:314] * np.float32(3e5))
+    note("varlen V beyond f16")
+    gpu = _run(torch, c, False, passes=("o",))
+    print(_check(gpu, c, False, label="varlen big V"))
+
