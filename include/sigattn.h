@@ -36,6 +36,14 @@
  *    matrix-core products instead of one), so that the result is limited by the
  *    bf16 inputs and the output type only. With fast_math = 1 a single bf16 value is
  *    used (relative rounding 2^-9 per weight) and the products cost half as much.
+ *    fast_math = 2 is the default's backward with an f16 forward: P is rounded once to
+ *    f16 (relative 2^-11; kept as 2^14 P, so normal down to P = 2^-28) and multiplied
+ *    with V converted to f16 (exact for |v| < 2^16; an item whose V holds a larger value
+ *    is computed again on hi + lo operands). Its error in an output row is about 2^-11
+ *    of that row's size, which meets max|err|/rms <= 2e-2 over a batch whose rows are of
+ *    similar size, but not over one that mixes sequences of very different lengths (a
+ *    row of a 2-token sequence next to those of an 8192-token one) or holds a few rows
+ *    much larger than the rest.
  *  - seqlens and bias are HOST arrays of length B, read during the call only.
  *    gate is a DEVICE array of floats, gate[b * gate_stride_b + j], j < Lmax.
  *  - The caller owns every buffer. The library never allocates, frees or
@@ -85,7 +93,8 @@ typedef struct sigattn_problem {
   int32_t B, H, Lmax, d;         /* 0 <= B <= 256, H >= 1, 1 <= Lmax <= 65535, d in {64,128} */
   int32_t dtype;                 /* sigattn_dtype of q, k, v, dO */
   int32_t out_dtype;             /* sigattn_dtype of o, dq, dk, dv (F32 when dtype is F32) */
-  int32_t fast_math;             /* 0: hi+lo split operands (default); 1: single bf16 */
+  int32_t fast_math;             /* 0: hi+lo split operands (default); 1: single bf16;
+                                     2: f16 P V in the forward, hi+lo in the backward */
   int64_t stride_b, stride_h, stride_l;  /* element strides, >= 0; d <= stride_l <= 2^22 */
   const int32_t* seqlens;        /* HOST [B]: valid length n_b, 0 <= n_b <= Lmax */
   int32_t causal;                /* 0: bidirectional; 1: key j allowed for query i iff j <= i */

@@ -159,6 +159,15 @@ def load():
     return lib
 
 
+def _fast_math(fast_math):
+    """False/0: hi + lo bf16 operands (default); True/1: single bf16; 2: f16 P V in the
+    forward (see the header's precision notes)."""
+    m = int(fast_math)
+    if m not in (0, 1, 2):
+        raise ValueError("fast_math must be 0 (or False), 1 (or True) or 2")
+    return m
+
+
 def make_problem(B, H, Lmax, d, seqlens, *, dtype=BF16, out_dtype=None, fast_math=False,
                  strides=None, causal=False, scale=0.0, bias=None, gate_ptr=None,
                  gate_stride_b=0, eps=1e-8, tau=0.0, sink=4):
@@ -173,7 +182,7 @@ def make_problem(B, H, Lmax, d, seqlens, *, dtype=BF16, out_dtype=None, fast_mat
     p.B, p.H, p.Lmax, p.d = B, H, Lmax, d
     p.dtype = dtype
     p.out_dtype = dtype if out_dtype is None else out_dtype
-    p.fast_math = 1 if fast_math else 0
+    p.fast_math = _fast_math(fast_math)
     p.stride_b, p.stride_h, p.stride_l = (int(s) for s in strides)
     p.seqlens = sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     p.causal = 1 if causal else 0
@@ -519,7 +528,7 @@ def _varlen_desc(q, k, tensors, cu_q, cu_k, max_q, max_k, causal, gate, tau, sin
     p.B, p.H, p.d = cu_q.numel() - 1, q.shape[1], q.shape[2]
     p.max_seqlen_q, p.max_seqlen_k = int(max_q), int(max_k)
     p.out_dtype = F32 if out_dtype == torch.float32 else BF16
-    p.fast_math = 1 if fast_math else 0
+    p.fast_math = _fast_math(fast_math)
     p.stride_t, p.stride_h = q.stride(0), q.stride(1)
     p.cu_seqlens_q, p.cu_seqlens_k = cu_q.data_ptr(), cu_k.data_ptr()
     p.causal = 1 if causal else 0

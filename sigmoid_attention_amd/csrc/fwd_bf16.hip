@@ -61,13 +61,16 @@ struct FwdOcc {
   static constexpr int value = (D == 64 && !RS) ? 3 : 2;
 };
 
-template <int D, int QB, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool RS, bool VL>
+// F16 (with SPLIT): P V on f16 operands where V fits, hi + lo bf16 otherwise.
+template <int D, int QB, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool RS, bool VL,
+          bool F16 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<D, QB, RS>::value, FwdOcc<D, QB, RS>::value)))
 void fwd_kernel(const KArgs a) {
+  static_assert(SPLIT || !F16, "f16 operands replace the hi + lo split");
   using T = FwdTraits<D, QB, CPT, GATED>;
   using Tile = DirectTile<T::BN, D, T::kWaves>;
   __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
-  // SPLIT: per ring slot, set when some value of that tile's V does not fit f16
+  // F16: per ring slot, set when some value of that tile's V does not fit f16
   __shared__ int vflag[T::NSTAGE];
 
   const int l = lane_id(), w = wave_id();
@@ -88,7 +91,9 @@ void fwd_kernel(const KArgs a) {
   const int item_q0 = it.t * T::BM;
   const int q0 = item_q0 + w * QB * 32;   // first query of this wave
   const float c1 = a.c1, c2 = it.c2;
-  const float c2s = c2 - 14.0f;   // exp2 argument of the 2^14-scaled logistic function
+  // F16 keeps P as 2^14 sigma: 14 comes off the exp2 argument, 2^-14 off the result
+  const float c2s = F16 ? c2 - 14.0f : c2;
+  const float out_scale = F16 ? kPScaleInv : 1.0f;
 
   // keys of the item: all of them, or (causal) those up to the item's last query + diag
   int kend = nk;
@@ -123,7 +128,7 @@ void fwd_kernel(const KArgs a) {
       tab[T::BN + l] = keep ? g : 0.0f;
     }
   };
-  // SPLIT: P V runs on f16 operands where V allows. P is kept as 2^14 sigma (in [0, 2^14],
+  // F16: P V runs on f16 operands where V allows. P is kept as 2^14 sigma (in [0, 2^14],
   // normal in f16 down to sigma = 2^-28) and rounded once to f16, 2^-11 relative, 8x
   // finer than bf16: one f16 product instead of the bf16 hi + lo pair. V's bf16 values
   // are exact in f16 below 2^16 in magnitude; during tile t each thread converts its two
@@ -158,7 +163,7 @@ void fwd_kernel(const KArgs a) {
     const bool bad = emax[0] >= 0x4780 || emax[1] >= 0x4780;
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && l == 0) vflag[t % T::NSTAGE] = 1;
   };
-  if (SPLIT && threadIdx.x < T::NSTAGE) vflag[threadIdx.x] = 0;
+  if (F16 && threadIdx.x < T::NSTAGE) vflag[threadIdx.x] = 0;
   if (ntiles > 0) {
     issue_tile(0);
     fill_table(0);
@@ -199,8 +204,8 @@ void fwd_kernel(const KArgs a) {
     for (int ks = 0; ks < T::KS; ++ks)
       s_cur = mfma(lds_row_operand<D>(smem, 0, 16 * ks), qop[0][ks], s_cur);
   }
-  int vbad = 0;   // SPLIT: some tile of this item had V beyond f16
-  if (SPLIT && ntiles > 0) {
+  int vbad = 0;   // f16 operands: some tile of this item had V beyond f16
+  if (F16 && ntiles > 0) {
     convert_v(0);
     __syncthreads();
   }
@@ -231,7 +236,8 @@ void fwd_kernel(const KArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = r0 + e;
-      float x = sigmoid_l2s(s_cur[r], c1, GATED ? tc2[e] : c2s);
+      float x = F16 ? sigmoid_l2s(s_cur[r], c1, GATED ? tc2[e] : c2s)
+                    : sigmoid_l2(s_cur[r], c1, GATED ? tc2[e] : c2s);
       if (MODE == kMasked) x = arc(r) <= lim ? x : 0.0f;
       if (RS) part += x;
       if (GATED) x *= tg[e];
@@ -263,7 +269,7 @@ void fwd_kernel(const KArgs a) {
   const LdsLane<D> lane;
   auto unit = [&](auto mode_tag, auto f16_tag, int qb, const char* Kn, int kn_row,
                   int qb_next, const char* Vt, int v_row, const float* tab, int kb) {
-    constexpr bool F16 = decltype(f16_tag)::value;
+    constexpr bool OPF16 = decltype(f16_tag)::value;
     bf16x8 kop[T::KS];
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) kop[ks] = lane.rowop(Kn, kn_row, ks);
@@ -280,7 +286,7 @@ void fwd_kernel(const KArgs a) {
     for (int ks = 0; ks < T::KS / 2; ++ks) s_next = mfma(kop[ks], qop[qb_next][ks], s_next);
     __builtin_amdgcn_sched_barrier(0);
     sig4(mode_tag, qb, 4, kb, tab, v_row, p);
-    if constexpr (F16) p16_0 = pack8_f16(p, 0);
+    if constexpr (OPF16) p16_0 = pack8_f16(p, 0);
     else to_bf16(p, 0, ph0, pl0);
 #pragma unroll
     for (int ks = T::KS / 2; ks < T::KS; ++ks) s_next = mfma(kop[ks], qop[qb_next][ks], s_next);
@@ -291,17 +297,17 @@ void fwd_kernel(const KArgs a) {
     sig4(mode_tag, qb, 8, kb, tab, v_row, p);
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) {
-      if constexpr (F16) acc[qb][dt] = mfma_f16(__builtin_bit_cast(f16x8, vop0[dt]), p16_0, acc[qb][dt]);
+      if constexpr (OPF16) acc[qb][dt] = mfma_f16(__builtin_bit_cast(f16x8, vop0[dt]), p16_0, acc[qb][dt]);
       else pv(qb, dt, vop0[dt], ph0, pl0);
     }
     __builtin_amdgcn_sched_barrier(0);
     sig4(mode_tag, qb, 12, kb, tab, v_row, p);
-    if constexpr (F16) p16_1 = pack8_f16(p, 8);
+    if constexpr (OPF16) p16_1 = pack8_f16(p, 8);
     else to_bf16(p, 1, ph1, pl1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) {
-      if constexpr (F16) acc[qb][dt] = mfma_f16(__builtin_bit_cast(f16x8, vop1[dt]), p16_1, acc[qb][dt]);
+      if constexpr (OPF16) acc[qb][dt] = mfma_f16(__builtin_bit_cast(f16x8, vop1[dt]), p16_1, acc[qb][dt]);
       else pv(qb, dt, vop1[dt], ph1, pl1);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -337,15 +343,15 @@ void fwd_kernel(const KArgs a) {
   auto tile_body = [&](auto mode_tag, auto stage_tag, auto f16_tag, int t) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr int SG = decltype(stage_tag)::value;
-    constexpr bool F16 = decltype(f16_tag)::value;
+    constexpr bool OPF16 = decltype(f16_tag)::value;
     if (t > 0) wait_vmem_and_barrier();
     const int st = SG >= 0 ? SG : t % T::NSTAGE;
     const int st1 = SG >= 0 ? (SG + 1) % T::NSTAGE : (t + 1) % T::NSTAGE;
     // every thread reads the flag after the barrier that follows all its writers
-    if constexpr (F16) vbad |= vflag[st];
+    if constexpr (OPF16) vbad |= vflag[st];
     if (t + 2 < ntiles) issue_tile(t + 2);
     if (t + 1 < ntiles) fill_table(t + 1);
-    if constexpr (F16) {
+    if constexpr (OPF16) {
       // tile t+2's slot was last read at the start of tile t-1
       if (threadIdx.x == 0) vflag[(st + 2) % T::NSTAGE] = 0;
       if (t + 1 < ntiles) convert_v(t + 1);
@@ -381,7 +387,7 @@ void fwd_kernel(const KArgs a) {
     for (; t < tmask; ++t) tile_body(Int{}, Dyn{}, f16_tag, t);
     for (; t < ntiles; ++t) tile_body(Msk{}, Dyn{}, f16_tag, t);
   };
-  if constexpr (SPLIT) {
+  if constexpr (F16) {
     tile_loops(Op16{});
     if (__builtin_amdgcn_readfirstlane(vbad)) {
       // again from the start on bf16 hi + lo operands: wait for the loads still in flight
@@ -414,7 +420,7 @@ void fwd_kernel(const KArgs a) {
       mass[qb] += __shfl_xor(mass[qb], 32, 64);
       const int query = q0 + 32 * qb + (l & 31);
       if (l < 32 && query < nq)
-        a.aux[((int64_t)it.b * a.H + it.h) * a.Lmax + query] = mass[qb] * kPScaleInv;
+        a.aux[((int64_t)it.b * a.H + it.h) * a.Lmax + query] = mass[qb] * out_scale;
     }
   }
 #pragma unroll
@@ -424,17 +430,25 @@ void fwd_kernel(const KArgs a) {
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
         store_row(a.out0, it.qoff + (int64_t)query * sl, a.out_f32, acc[qb][dt], 32 * dt,
-                  kPScaleInv);
+                  out_scale);
     }
   }
 }
 
 template <int D, int QB, int CPT, bool C, bool G, bool SP, bool RS>
 static hipError_t launch_one(const KArgs& a, hipStream_t st) {
+  const dim3 grid(a.nitems), block(256);
+  if constexpr (SP) {
+    if (a.f16_pv) {
+      if (a.varlen) hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, true, false, true, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, true, RS, false, true>), grid, block, 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (a.varlen)
-    hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP, false, true>), dim3(a.nitems), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP, false, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP, RS, false>), dim3(a.nitems), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<D, QB, CPT, C, G, SP, RS, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ struct KArgs {
   int32_t reverse;       // list tiles last-first (causal query-side passes)
   int32_t gate_sink;
   int32_t out_f32;       // outputs are float (else bf16)
+  int32_t f16_pv;        // forward with hi+lo operands: P V on f16 operands where V fits
   float c1;              // -s * log2(e): logit scale folded into the exp2 argument
   float scale;           // s
   float gate_eps;

@@ -66,7 +66,7 @@ sigattn_status validate_problem(const sigattn_problem* p) {
   if (p->dtype != SIGATTN_BF16 && p->dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
   if (p->out_dtype != SIGATTN_BF16 && p->out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
   if (p->dtype == SIGATTN_F32 && p->out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
-  if (p->fast_math != 0 && p->fast_math != 1) return SIGATTN_ERR_INVALID_ARG;
+  if (p->fast_math < 0 || p->fast_math > 2) return SIGATTN_ERR_INVALID_ARG;
   if (p->stride_b < 0 || p->stride_h < 0 || p->stride_l < p->d) return SIGATTN_ERR_INVALID_ARG;
   // tile loads address up to 128 rows from a per-tile base with 32-bit byte offsets
   if (p->stride_l > SIGATTN_MAX_ROW_STRIDE) return SIGATTN_ERR_UNSUPPORTED;
@@ -168,6 +168,7 @@ void plan_pass(const sigattn_problem* p, int pass, KArgs* a) {
   a->gate_tau = p->gate_tau;
   a->gate_sink = p->gate_sink;
   a->out_f32 = p->out_dtype == SIGATTN_F32 ? 1 : 0;
+  a->f16_pv = (pass == 0 && p->fast_math == 2) ? 1 : 0;
 }
 
 bool needs_zero_fill(const sigattn_problem* p) {
@@ -248,7 +249,7 @@ sigattn_status run_pass(const sigattn_problem* p, int pass, const void* q, const
   const bool causal = p->causal != 0, gated = p->gate != nullptr;
   if (a.nitems > 0) {
     hipError_t e;
-    const bool split = p->fast_math == 0;
+    const bool split = p->fast_math != 1;
     if (pass == 0) e = sa::launch_fwd_bf16(a, p->d, causal, gated, split, st);
     else if (pass == 1) e = sa::launch_dq_bf16(a, p->d, causal, gated, split, st);
     else e = sa::launch_dkdv_bf16(a, p->d, causal, gated, split, st);
@@ -276,7 +277,7 @@ sigattn_status validate_varlen(const sigattn_varlen* p) {
     return SIGATTN_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return SIGATTN_ERR_UNSUPPORTED;
   if (p->out_dtype != SIGATTN_BF16 && p->out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
-  if (p->fast_math != 0 && p->fast_math != 1) return SIGATTN_ERR_INVALID_ARG;
+  if (p->fast_math < 0 || p->fast_math > 2) return SIGATTN_ERR_INVALID_ARG;
   if (p->causal != 0 && p->causal != 1) return SIGATTN_ERR_INVALID_ARG;
   if (p->stride_t < 0 || p->stride_h < 0) return SIGATTN_ERR_INVALID_ARG;
   if (p->stride_t > SIGATTN_MAX_ROW_STRIDE) return SIGATTN_ERR_UNSUPPORTED;
@@ -330,6 +331,7 @@ void plan_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k
   a.gate_sink = p->gate_sink;
   a.out_f32 = p->out_dtype == SIGATTN_F32 ? 1 : 0;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1;
+  a.f16_pv = (pass == 0 && p->fast_math == 2) ? 1 : 0;
 }
 
 sigattn_status run_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k,
@@ -338,7 +340,7 @@ sigattn_status run_varlen(const sigattn_varlen* p, int pass, const void* q, cons
   plan_varlen(p, pass, q, k, v, dout, o0, o1, a);
   if (a.nitems == 0) return SIGATTN_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool causal = p->causal != 0, gated = p->gate != nullptr, split = p->fast_math == 0;
+  const bool causal = p->causal != 0, gated = p->gate != nullptr, split = p->fast_math != 1;
   hipError_t e;
   if (pass == 0) e = sa::launch_fwd_bf16(a, p->d, causal, gated, split, st);
   else if (pass == 1) e = sa::launch_dq_bf16(a, p->d, causal, gated, split, st);
@@ -472,7 +474,7 @@ sigattn_status sigattn_bwd(const sigattn_problem* p, const void* q, const void* 
   plan_pass(p, 2, &a);
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = dk; a.out1 = dv;
   if (a.nitems > 0 && sa::launch_bwd_bf16(a, dq, a.nitems, 0, p->causal != 0, p->gate != nullptr,
-                                          p->fast_math == 0, st) != hipSuccess)
+                                          p->fast_math != 1, st) != hipSuccess)
     return SIGATTN_ERR_HIP;
   if ((s = zero_fill(p, dk, dv, st)) != SIGATTN_OK) return s;
   return zero_fill(p, dq, nullptr, st);
@@ -546,7 +548,7 @@ sigattn_status sigattn_bwd_varlen(const sigattn_varlen* p, const void* q, const 
   const int nq_items = (int)((int64_t)p->B * p->H * tiles_q);
   if (a.nitems + nq_items == 0) return SIGATTN_OK;
   return sa::launch_bwd_bf16(a, dq, nq_items, tiles_q, p->causal != 0, p->gate != nullptr,
-                             p->fast_math == 0, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+                             p->fast_math != 1, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? SIGATTN_OK : SIGATTN_ERR_HIP;
 }
 

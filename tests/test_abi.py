@@ -69,7 +69,9 @@ def _prob(**kw):
     (lambda p: setattr(p, "dtype", 7), 2),
     (lambda p: setattr(p, "out_dtype", 5), 2),
     (lambda p: (setattr(p, "dtype", 1), setattr(p, "out_dtype", 0)), 2),
-    (lambda p: setattr(p, "fast_math", 2), 1),
+    (lambda p: setattr(p, "fast_math", 3), 1),
+    (lambda p: setattr(p, "fast_math", -1), 1),
+    (lambda p: setattr(p, "fast_math", 2), 0),
     (lambda p: setattr(p, "causal", 2), 1),
     (lambda p: setattr(p, "stride_l", 32), 1),
     (lambda p: setattr(p, "stride_l", 68), 3),      # 136-byte rows: not 16-byte aligned

@@ -181,8 +181,9 @@ def test_full_size_sampled(name):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 def test_values_beyond_f16(d, causal):
-    """V values beyond the f16 range (|v| >= 2^16) in some tiles: those items run again
-    on bf16 hi + lo operands; everything still meets the stated bar, padded rows 0."""
+    """fast_math = 2 with V values beyond the f16 range (|v| >= 2^16) in some tiles: those
+    items run again on bf16 hi + lo operands; everything still meets the stated bar,
+    padded rows 0 (and the default mode, which never converts V, too)."""
     torch = need_gpu()
     w = W.Workload(f"big_v_{d}", "bf16", 3, 2, d, 600, ("fixed", [600, 333, 65]),
                    seed=700 + d + causal, causal=causal)
@@ -193,8 +194,44 @@ def test_values_beyond_f16(d, causal):
     v[1, 0, 5, 3] = np.float32(65280.0)           # the largest bf16 below 2^16 stays f16
     data["v"] = W.round_to_bf16(v)
     ref, mag = oracle_full(data), oracle_magnitudes(data)
-    note(f"V beyond f16 d={d} causal={causal}")
-    gpu = run_gpu(data, torch.bfloat16, out_dtype=torch.float32)
-    print(check_all(gpu, ref, data["seqlens"], BF16_TOL, f"big V {d}"))
-    print(check_bounds(gpu, ref, mag, data["seqlens"], False, False, f"big V {d}"))
+    for mode in (2, 0):
+        note(f"V beyond f16 d={d} causal={causal} fast_math={mode}")
+        gpu = run_gpu(data, torch.bfloat16, out_dtype=torch.float32, fast_math=mode)
+        print(check_all(gpu, ref, data["seqlens"], BF16_TOL, f"big V {d}"))
+        print(check_bounds(gpu, ref, mag, data["seqlens"], False, False, f"big V {d}", f16=mode == 2))
+
+
+@pytest.mark.parametrize("variant", list(SMALL_VARIANTS))
+@pytest.mark.parametrize("d", [64, 128])
+def test_f16_forward_mode(d, variant):
+    """fast_math = 2 (P V on f16 operands in the forward, hi + lo backward): the stated
+    bar and the f16 bound on the forward output for ragged batches whose rows are of
+    similar size; dQ, dK, dV bitwise those of the default mode."""
+    torch = need_gpu()
+    w = W.Workload(f"f16mode_{variant}_{d}", "bf16", 4, 3, d, 700, ("fixed", [700, 333, 129, 600]),
+                   seed=740 + d, **SMALL_VARIANTS[variant])
+    data = W.generate(w)
+    ref, mag = oracle_full(data), oracle_magnitudes(data)
+    note(f"f16 forward mode d={d} {variant}")
+    gpu = run_gpu(data, torch.bfloat16, out_dtype=torch.float32, fast_math=2)
+    print(check_all(gpu, ref, data["seqlens"], BF16_TOL, f"f16 mode {variant} {d}"))
+    print(check_bounds(gpu, ref, mag, data["seqlens"], False, False, f"f16 mode {variant} {d}", f16=True))
+    base = run_gpu(data, torch.bfloat16, passes=("dq", "dkdv"), out_dtype=torch.float32)
+    for name in ("dQ", "dK", "dV"):
+        assert np.array_equal(gpu[name], base[name]), f"{name} differs from the default mode"
+
+
+def test_f16_forward_mode_long_sampled():
+    """fast_math = 2 at the benchmark shape (long_8k_s1), sampled rows against the oracle."""
+    torch = need_gpu()
+    data = W.generate(W.WORKLOADS["long_8k_s1"])
+    note("f16 forward mode long_8k_s1")
+    gpu = run_gpu(data, torch.bfloat16, passes=("o",), out_dtype=torch.float32, fast_math=2)
+    sl = data["seqlens"]
+    for b, h in ((0, 0), (3, 5)):
+        n = int(sl[b])
+        rows = np.array([0, 1, 127, 128, n // 2, n - 1])
+        ref = O.forward_rows(data["q"], data["k"], data["v"], sl, b, h, rows)
+        e = err_ratio(gpu["O"][b, h, rows], ref, np.ones(ref.shape, bool))
+        assert e <= BF16_TOL, f"long_8k_s1 f16 mode b={b} h={h}: {e:.3e}"
 
