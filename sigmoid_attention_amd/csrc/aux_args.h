@@ -11,8 +11,10 @@ constexpr int kZeroRows = 32;
 struct ZArgs {
   void* o0;
   void* o1;              // second output or null
+  void* o2;              // third output or null
   int64_t sb, sh, sl;    // element strides
   int32_t Lmax;
+  int32_t block0;        // first row block holding a padded row (shortest sequence's)
   int32_t row_bytes;     // d * element size (a multiple of 16)
   int32_t esize;         // element size in bytes
   uint16_t len[kMaxBatch];   // valid length by batch index

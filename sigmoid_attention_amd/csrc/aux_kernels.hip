@@ -1,6 +1,8 @@
 // Auxiliary kernels:
-//  * zero_rows: writes exact zeros into the padded rows (i >= n_b) of one or two
-//    outputs, so that every output element is defined. Padded input slots are never
+//  * zero_rows: writes exact zeros into the padded rows (i >= n_b) of up to three
+//    outputs, so that every output element is defined. The grid starts at the row block
+//    of the shortest sequence's first padded row; blocks below a longer sequence's
+//    length exit at once. Padded input slots are never
 //    read (padded tiles are skipped, "Better Models, Faster Training: Sigmoid Attention
 //    for single-cell Foundation Models", section 4).
 //  * plane_tail: per-head float planes [B][H][Lmax] (gate gradient, row mass): zeros
@@ -21,7 +23,7 @@ namespace sa {
 __global__ __launch_bounds__(256) void zero_rows_kernel(const ZArgs z) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int n = z.len[b];
-  const int row0 = blockIdx.x * kZeroRows;
+  const int row0 = (z.block0 + blockIdx.x) * kZeroRows;
   if (row0 + kZeroRows <= n) return;
   const int cpr = z.row_bytes / 16;
   const int64_t hoff = ((int64_t)b * z.sb + (int64_t)h * z.sh) * z.esize;
@@ -32,11 +34,12 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(const ZArgs z) {
     const uint4 zero = {0u, 0u, 0u, 0u};
     *reinterpret_cast<uint4*>((char*)z.o0 + off) = zero;
     if (z.o1) *reinterpret_cast<uint4*>((char*)z.o1 + off) = zero;
+    if (z.o2) *reinterpret_cast<uint4*>((char*)z.o2 + off) = zero;
   }
 }
 
 hipError_t launch_zero_rows(const ZArgs& z, int B, int H, hipStream_t st) {
-  dim3 grid((z.Lmax + kZeroRows - 1) / kZeroRows, H, B);
+  dim3 grid((z.Lmax + kZeroRows - 1) / kZeroRows - z.block0, H, B);
   hipLaunchKernelGGL(zero_rows_kernel, grid, dim3(256), 0, st, z);
   return hipGetLastError();
 }

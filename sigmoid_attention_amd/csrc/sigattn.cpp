@@ -177,12 +177,17 @@ bool needs_zero_fill(const sigattn_problem* p) {
   return false;
 }
 
-sigattn_status zero_fill(const sigattn_problem* p, void* o0, void* o1, hipStream_t st) {
+sigattn_status zero_fill(const sigattn_problem* p, void* o0, void* o1, hipStream_t st,
+                         void* o2 = nullptr) {
   if (!needs_zero_fill(p)) return SIGATTN_OK;
   sa::ZArgs z;
   std::memset(&z, 0, sizeof(z));
   z.o0 = o0;
   z.o1 = o1;
+  z.o2 = o2;
+  int nmin = p->Lmax;
+  for (int b = 0; b < p->B; ++b) nmin = p->seqlens[b] < nmin ? p->seqlens[b] : nmin;
+  z.block0 = nmin / sa::kZeroRows;   // nmin < Lmax here, so at least one block remains
   z.sb = p->stride_b;
   z.sh = p->stride_h;
   z.sl = p->stride_l;
@@ -476,8 +481,7 @@ sigattn_status sigattn_bwd(const sigattn_problem* p, const void* q, const void* 
   if (a.nitems > 0 && sa::launch_bwd_bf16(a, dq, a.nitems, 0, p->causal != 0, p->gate != nullptr,
                                           p->fast_math != 1, st) != hipSuccess)
     return SIGATTN_ERR_HIP;
-  if ((s = zero_fill(p, dk, dv, st)) != SIGATTN_OK) return s;
-  return zero_fill(p, dq, nullptr, st);
+  return zero_fill(p, dk, dv, st, dq);
 }
 
 sigattn_status sigattn_bwd_dkdv_dg(const sigattn_problem* p, const void* q, const void* k,
