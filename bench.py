@@ -397,6 +397,15 @@ def main():
     res = measure(S, W, w, t, gate, sl, stream, args.steps, args.warmup, out_dtype,
                   fast_math)
     res["mode"] = mode
+    # the bf16 MFMA rate and shader clock this GPU sustains in a register-only MFMA loop:
+    # the measured counterpart of the published peak (the attention kernels run at their
+    # own, lower clock under load)
+    cal = S.calibrate_mfma()
+    res["mfma_peak_measured"] = {
+        "tflops": cal["tflops"], "sclk_mhz": cal["sclk_mhz"],
+        "kernel": "sigattn_calibrate_mfma: v_mfma_f32_32x32x16_bf16 loop, 4 accumulators",
+        "dominant_frac": res["roofline"]["achieved"] / cal["tflops"],
+        "fwd_frac": res["fwd_tflops"] / cal["tflops"]}
     if fast_math == 0:
         # the opt-in f16 forward beside the default (same step, same inputs)
         f16 = measure(S, W, w, t, gate, sl, stream, args.steps, args.warmup, out_dtype, 2)

@@ -301,6 +301,25 @@ sigattn_status sigattn_decode(const sigattn_cache* c, const void* q, int64_t str
 int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int64_t cap,
                      int32_t* tile_rows);
 
+/* Measurement aid (no attention work): the bf16 MFMA rate and shader clock this GPU
+ * sustains, against which the attention kernels' throughput is also reported. Launches
+ * nblocks workgroups of 256 threads on `stream`; every wave runs `iters` iterations of 16
+ * v_mfma_f32_32x32x16_bf16 on four independent register accumulators, with no memory
+ * traffic in the loop. sink: DEVICE float [nblocks * 256], 4-byte aligned, one value
+ * per thread that keeps the products live (contents meaningless). clk: DEVICE int64
+ * [2 * nblocks], 8-byte aligned: per workgroup, its elapsed shader-clock cycles
+ * (s_memtime) and 100 MHz ticks (s_memrealtime); sum(cycles) / sum(ticks) * 100 is
+ * the clock in MHz. Both buffers are owned by the caller and valid once the stream is
+ * synchronised. 1 <= nblocks <= SIGATTN_MAX_CALIB_BLOCKS and 1 <= iters <=
+ * SIGATTN_MAX_CALIB_ITERS, else SIGATTN_ERR_INVALID_ARG; misaligned buffers give
+ * SIGATTN_ERR_ALIGNMENT. Nothing is enqueued on error. */
+#define SIGATTN_MAX_CALIB_BLOCKS (1 << 16)
+#define SIGATTN_MAX_CALIB_ITERS (1 << 20)
+sigattn_status sigattn_calibrate_mfma(int32_t nblocks, int32_t iters, float* sink,
+                                      int64_t* clk, void* stream);
+/* The matrix-core flops one sigattn_calibrate_mfma call performs (0 for invalid sizes). */
+double sigattn_calibrate_mfma_flops(int32_t nblocks, int32_t iters);
+
 const char* sigattn_status_string(sigattn_status s);
 int sigattn_version(void);
 

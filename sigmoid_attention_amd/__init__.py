@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd", "bwd_dkdv_dg", "fwd_varlen",
            "bwd_dq_varlen", "bwd_dkdv_varlen", "bwd_varlen", "VarlenDesc", "KVCache",
-           "CacheDesc", "validate", "plan", "library_path", "load",
+           "CacheDesc", "validate", "plan", "calibrate_mfma", "library_path", "load",
            "Problem", "SigattnError", "STATUS", "VERSION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -107,6 +107,32 @@ class CacheDesc(ctypes.Structure):
 _lib = None
 
 
+def calibrate_mfma(nblocks: int = 2048, iters: int = 4096, device=None) -> dict:
+    """The bf16 MFMA rate and shader clock this GPU sustains (sigattn_calibrate_mfma):
+    one timed launch on the current stream after one warm-up launch. Returns the flops,
+    the launch time in ms (HIP events), TFLOP/s and the mean clock in MHz from the
+    per-workgroup shader-cycle and 100 MHz stamps."""
+    torch = _torch()
+    lib = load()
+    dev = torch.device(device if device is not None else "cuda")
+    sink = torch.empty(nblocks * 256, dtype=torch.float32, device=dev)
+    clk = torch.empty(2 * nblocks, dtype=torch.int64, device=dev)
+    st = torch.cuda.current_stream(dev)
+    _check(lib.sigattn_calibrate_mfma(nblocks, iters, sink.data_ptr(), clk.data_ptr(),
+                                      st.cuda_stream), "sigattn_calibrate_mfma")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    _check(lib.sigattn_calibrate_mfma(nblocks, iters, sink.data_ptr(), clk.data_ptr(),
+                                      st.cuda_stream), "sigattn_calibrate_mfma")
+    e1.record(st)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    c = clk.view(nblocks, 2).double().sum(0).cpu().numpy()
+    flops = lib.sigattn_calibrate_mfma_flops(nblocks, iters)
+    return {"flops": flops, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "sclk_mhz": float(c[0] / c[1] * 100.0), "nblocks": nblocks, "iters": iters}
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -152,6 +178,10 @@ def load():
     lib.sigattn_status_string.argtypes = [ctypes.c_int]
     lib.sigattn_status_string.restype = ctypes.c_char_p
     lib.sigattn_version.restype = ctypes.c_int
+    lib.sigattn_calibrate_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    lib.sigattn_calibrate_mfma.restype = ctypes.c_int
+    lib.sigattn_calibrate_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.sigattn_calibrate_mfma_flops.restype = ctypes.c_double
     for f in (lib.sigattn_validate, lib.sigattn_fwd, lib.sigattn_fwd_rowsum, lib.sigattn_bwd_dq,
               lib.sigattn_bwd_dkdv, lib.sigattn_bwd, lib.sigattn_bwd_dkdv_dg):
         f.restype = ctypes.c_int

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libsigattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["fwd_bf16.hip", "bwd_dq_bf16.hip", "bwd_dkdv_bf16.hip", "bwd_fused_bf16.hip",
-           "aux_kernels.hip", "decode_bf16.hip", "sigattn.cpp"]
+           "aux_kernels.hip", "decode_bf16.hip", "calib.hip", "sigattn.cpp"]
 
 # gfx950 only; packed fp32 VALU instructions are disabled (hipcc's host pass warns
 # that it does not know the feature, which is harmless).

@@ -32,6 +32,8 @@ hipError_t launch_f32(const DArgs& a, int pass, hipStream_t st);
 hipError_t launch_cache_build(const BuildArgs& a, int B, hipStream_t st);
 hipError_t launch_cache_append(const AppendArgs& a, int B, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+int calib_mfma_per_iter();
+hipError_t launch_mfma_calib(float* sink, int64_t* clk, int nblocks, int iters, hipStream_t st);
 }  // namespace sa
 
 namespace {
@@ -682,6 +684,25 @@ int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int
     items[3 * w + 2] = it.t;
   }
   return a.nitems;
+}
+
+sigattn_status sigattn_calibrate_mfma(int32_t nblocks, int32_t iters, float* sink,
+                                      int64_t* clk, void* stream) {
+  if (nblocks < 1 || nblocks > SIGATTN_MAX_CALIB_BLOCKS || iters < 1 ||
+      iters > SIGATTN_MAX_CALIB_ITERS || !sink || !clk)
+    return SIGATTN_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u) || (reinterpret_cast<uintptr_t>(clk) & 7u))
+    return SIGATTN_ERR_ALIGNMENT;
+  return sa::launch_mfma_calib(sink, clk, nblocks, iters, reinterpret_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? SIGATTN_OK
+             : SIGATTN_ERR_HIP;
+}
+
+double sigattn_calibrate_mfma_flops(int32_t nblocks, int32_t iters) {
+  if (nblocks < 1 || iters < 1) return 0.0;
+  // 4 waves per workgroup; 32 x 32 x 16 products, 2 flops each
+  return (double)nblocks * 4.0 * (double)iters * sa::calib_mfma_per_iter() * 32.0 * 32.0 * 16.0 * 2.0;
 }
 
 const char* sigattn_status_string(sigattn_status s) {
