@@ -310,11 +310,13 @@ int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int
  * [2 * nblocks], 8-byte aligned: per workgroup, its elapsed shader-clock cycles
  * (s_memtime) and 100 MHz ticks (s_memrealtime); sum(cycles) / sum(ticks) * 100 is
  * the clock in MHz. Both buffers are owned by the caller and valid once the stream is
- * synchronised. 1 <= nblocks <= SIGATTN_MAX_CALIB_BLOCKS and 1 <= iters <=
- * SIGATTN_MAX_CALIB_ITERS, else SIGATTN_ERR_INVALID_ARG; misaligned buffers give
- * SIGATTN_ERR_ALIGNMENT. Nothing is enqueued on error. */
+ * synchronised. 1 <= nblocks <= SIGATTN_MAX_CALIB_BLOCKS, 1 <= iters <=
+ * SIGATTN_MAX_CALIB_ITERS and nblocks * iters <= SIGATTN_MAX_CALIB_WORK (a launch of at
+ * most a few tens of milliseconds), else SIGATTN_ERR_INVALID_ARG; misaligned buffers
+ * give SIGATTN_ERR_ALIGNMENT. Nothing is enqueued on error. */
 #define SIGATTN_MAX_CALIB_BLOCKS (1 << 16)
 #define SIGATTN_MAX_CALIB_ITERS (1 << 20)
+#define SIGATTN_MAX_CALIB_WORK (1LL << 24)
 sigattn_status sigattn_calibrate_mfma(int32_t nblocks, int32_t iters, float* sink,
                                       int64_t* clk, void* stream);
 /* The matrix-core flops one sigattn_calibrate_mfma call performs (0 for invalid sizes). */

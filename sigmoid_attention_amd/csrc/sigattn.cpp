@@ -689,7 +689,8 @@ int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int
 sigattn_status sigattn_calibrate_mfma(int32_t nblocks, int32_t iters, float* sink,
                                       int64_t* clk, void* stream) {
   if (nblocks < 1 || nblocks > SIGATTN_MAX_CALIB_BLOCKS || iters < 1 ||
-      iters > SIGATTN_MAX_CALIB_ITERS || !sink || !clk)
+      iters > SIGATTN_MAX_CALIB_ITERS || (int64_t)nblocks * iters > SIGATTN_MAX_CALIB_WORK ||
+      !sink || !clk)
     return SIGATTN_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(sink) & 3u) || (reinterpret_cast<uintptr_t>(clk) & 7u))
     return SIGATTN_ERR_ALIGNMENT;

@@ -12,6 +12,7 @@ def test_calibrate_rejects_bad_arguments():
     assert lib.sigattn_calibrate_mfma(1, 1, None, None, None) == 1
     assert lib.sigattn_calibrate_mfma((1 << 16) + 1, 1, 16, 16, None) == 1
     assert lib.sigattn_calibrate_mfma(1, (1 << 20) + 1, 16, 16, None) == 1
+    assert lib.sigattn_calibrate_mfma(1 << 16, 1 << 9, 16, 16, None) == 1   # over 2^24 in all
     assert lib.sigattn_calibrate_mfma(1, 1, 18, 16, None) == 3     # sink not 4-byte aligned
     assert lib.sigattn_calibrate_mfma(1, 1, 16, 12, None) == 3     # clk not 8-byte aligned
 
