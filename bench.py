@@ -216,6 +216,26 @@ def measure_decode(S, W, w, steps, warmup, no_cpu, cpu_seconds):
                      "traffic": traffic_for(w.name, "decode")},
         "algorithmic_bytes": nbytes,
     }
+    # a plain streaming read + write of the same order of size (torch's float32 multiply,
+    # the kernel the traffic counters are calibrated on): the measured counterpart of the
+    # published HBM peak
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    cp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(20)]
+    for e0, e1 in cp:
+        e0.record(stream)
+        torch.mul(src, 2.0, out=dst)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_cp = float(np.median([e0.elapsed_time(e1) for e0, e1 in cp]))
+    cp_gbs = 2 * COPY_ELEMS * 4 / (ms_cp * 1e-3) / 1e9
+    res["hbm_stream_measured"] = {
+        "gbs": cp_gbs, "kernel": "torch float32 multiply, 256 MiB read + 256 MiB written",
+        "decode_frac": res["roofline"]["achieved"] / cp_gbs}
+    del src, dst
     if not no_cpu:
         res["cpu_baseline"] = cpu_baseline_decode(data, w, bias, cpu_seconds)
     return res
