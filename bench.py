@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long_8k_s1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-padding-line", action="store_true",
+                    help="skip the 0 %% / 25 %% padding pair reported beside the headline")
     ap.add_argument("--fast-math", action="store_true",
                     help="time the single-bf16 operand mode instead of the default hi+lo split")
     ap.add_argument("--f16-forward", action="store_true",
@@ -72,6 +74,18 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="lower bound on the oracle time of the CPU baseline sample")
     return ap.parse_args()
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), else the platform's description."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def cpu_baseline(data, w, min_seconds):
@@ -125,7 +139,7 @@ def cpu_baseline(data, w, min_seconds):
         "kind": "oracle",
         "sample": f"fp64 numpy oracle, forward+backward of {parts} of {w.name}; "
                   f"fwd {t_fwd:.2f} s, bwd {t_bwd:.2f} s",
-        "host": platform.processor() or platform.machine(),
+        "host": cpu_model(),
         "host_cpus": os.cpu_count(),
     }
 
@@ -155,7 +169,7 @@ def cpu_baseline_decode(data, w, bias, min_seconds):
             "kind": "oracle",
             "sample": f"fp64 numpy oracle decode of {seqs} of the {w.B} sequences of {w.name} "
                       f"(all heads), {t_dec:.2f} s; cache compaction untimed",
-            "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+            "host": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def decode_bytes(counts, H, d, out_bytes):
@@ -435,6 +449,8 @@ def main():
             "fwd_ms": f16["kernels"]["fwd"]["avg_ms"],
             "note": "P V on f16 operands in the forward (P rounded to f16, 2^-11); meets "
                     "the stated bar when the batch's output rows are of similar size"}
+    if not args.no_padding_line:
+        res["padding_loss"] = padding_loss(S, W, stream, 20, 5, out_dtype, fast_math)
     if args.also_fast:
         fast = measure(S, W, w, t, gate, sl, stream, args.steps, args.warmup,
                        torch.bfloat16, True)
@@ -443,6 +459,35 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(data, w, args.cpu_seconds)
     print(json.dumps(res))
+
+
+def padding_loss(S, W, stream, steps, warmup, out_dtype, fast_math):
+    """The padding target's workload pair (B = 16, H = 16, d = 128, Lmax = 4096, mean
+    padding 0 % and 25 %; the valid lengths of pad_sweep_0 and pad_sweep_25), one step =
+    sigattn_fwd + sigattn_bwd as in the headline line, effective TFLOPS over valid tokens
+    and the loss from 0 % to 25 %. Timing only: the values are standard normals drawn on
+    the GPU with torch's seeded generator (the kernels' work does not depend on them)."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = {}
+    for name in ("pad_sweep_0", "pad_sweep_25"):
+        w = W.WORKLOADS[name]
+        sl = W.seqlens_of(w)
+        g = torch.Generator(device=dev).manual_seed(w.seed)
+        t = {k_: torch.randn((w.B, w.H, w.L, w.d), generator=g, device=dev).to(torch.bfloat16)
+             for k_ in ("q", "k", "v", "do")}
+        m = measure(S, W, w, t, None, sl, stream, steps, warmup, out_dtype, fast_math,
+                    separate=False)
+        out[name] = {"padding": float(1.0 - np.mean(sl) / w.L), "value": m["value"],
+                     "ms_per_step": m["ms_per_step"], "fwd_tflops": m["fwd_tflops"],
+                     "bwd_tflops": m["bwd_tflops"]}
+        del t
+        torch.cuda.empty_cache()
+    a, b = out["pad_sweep_0"], out["pad_sweep_25"]
+    out["loss_pct"] = {k_: 100.0 * (1.0 - b[k_] / a[k_])
+                       for k_ in ("value", "fwd_tflops", "bwd_tflops")}
+    out["target"] = "effective TFLOPS loss from 0 % to 25 % padding below 10 %"
+    return out
 
 
 def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False):
@@ -591,7 +636,7 @@ def measure_packed(S, W, w, data, stream, steps, warmup, out_dtype, fast_math):
     }
 
 
-def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):
+def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math, separate=True):
     import torch
     kw = dict(causal=w.causal, gate=gate, tau=w.tau, sink=w.sink, out_dtype=out_dtype,
               fast_math=fast_math)
@@ -633,7 +678,7 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math):
     # one-call backward runs in one launch
     sep = {"bwd_dq": lambda: S.bwd_dq(t["q"], t["k"], t["v"], t["do"], sl, out=dq, **kw),
            "bwd_dkdv": lambda: S.bwd_dkdv(t["q"], t["k"], t["v"], t["do"], sl, out=(dk, dv), **kw)}
-    for name, fn in sep.items():
+    for name, fn in (sep.items() if separate else ()):
         for _ in range(max(2, warmup // 4)):
             fn()
         pairs_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

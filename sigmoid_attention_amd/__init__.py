@@ -220,6 +220,8 @@ def make_problem(B, H, Lmax, d, seqlens, *, dtype=BF16, out_dtype=None, fast_mat
     keep = [sl]
     if bias is not None:
         bb = np.ascontiguousarray(np.asarray(bias, dtype=np.float32).reshape(-1))
+        if bb.shape[0] != B:
+            raise ValueError(f"bias has {bb.shape[0]} entries, expected B = {B}")
         keep.append(bb)
         p.bias = bb.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
     p.gate = gate_ptr
@@ -265,8 +267,6 @@ def _describe(q, tensors, seqlens, causal, gate, tau, sink, eps, scale, bias,
     for t in tensors:
         if t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype:
             raise ValueError("all tensors must share shape, strides and dtype")
-        if t.device != q.device or t.device.type != "cuda":
-            raise ValueError("all tensors must be on the same GPU")
     if q.stride(-1) != 1:
         raise ValueError("the last dimension must be contiguous")
     if q.dtype == torch.bfloat16:
@@ -277,11 +277,14 @@ def _describe(q, tensors, seqlens, causal, gate, tau, sink, eps, scale, bias,
         raise ValueError("dtype must be bfloat16 or float32")
     gate_ptr, gsb = None, 0
     if gate is not None:
-        if gate.dtype != torch.float32 or gate.device != q.device or gate.dim() != 2:
-            raise ValueError("gate must be a float32 [B, Lmax] tensor on the same GPU")
-        if gate.stride(-1) != 1:
-            raise ValueError("gate rows must be contiguous")
+        if gate.dtype != torch.float32 or gate.dim() != 2 or tuple(gate.shape) != (B, L):
+            raise ValueError(f"gate must be a float32 [B, Lmax] = [{B}, {L}] tensor")
+        if gate.stride(-1) != 1 or (B > 1 and gate.stride(0) < L):
+            raise ValueError("gate rows must be contiguous and must not overlap")
         gate_ptr, gsb = gate.data_ptr(), gate.stride(0)
+    for t in (q,) + tuple(tensors) + (() if gate is None else (gate,)):
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError("all tensors must be on the same GPU")
     if hasattr(seqlens, "cpu"):
         seqlens = seqlens.cpu().numpy()
     if out_dtype is None or out_dtype == q.dtype:
@@ -498,6 +501,16 @@ class KVCache:
         self._new_rows_ok(v_new, "v_new")
         if k_new.stride() != v_new.stride():
             raise ValueError("k_new and v_new must share strides")
+        torch = _torch()
+        B = self.shape[0]
+        if (self.gate is None) != (g_new is None):
+            raise ValueError("g_new is required exactly when the cache has gates")
+        if g_new is not None and (g_new.dtype != torch.float32 or tuple(g_new.shape) != (B,)
+                                  or not g_new.is_contiguous() or g_new.device != self.k.device):
+            raise ValueError("g_new must be a contiguous float32 [B] tensor on the cache's GPU")
+        if status is not None and (status.dtype != torch.int32 or status.numel() < 1
+                                   or status.device != self.k.device):
+            raise ValueError("status must be an int32 tensor on the cache's GPU")
         lib = load()
         code = lib.sigattn_cache_append(
             ctypes.byref(self.desc), k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0),
@@ -508,29 +521,42 @@ class KVCache:
     def workspace_size(self) -> int:
         return int(load().sigattn_decode_workspace_size(ctypes.byref(self.desc)))
 
-    def decode(self, q, bias, *, scale=0.0, out=None, out_dtype=None, workspace=None):
-        """o[b, h] = sum over live entries of sigma(s q.k + beta_b [+ log(g+eps)]) [g] v.
-        bias: host sequence of B floats (beta_b)."""
+    def _decode_args(self, q, bias, out, out_dtype):
         torch = _torch()
         self._new_rows_ok(q, "q")
-        lib = load()
         B = self.shape[0]
         bb = np.ascontiguousarray(np.asarray(bias, dtype=np.float32).reshape(-1))
         if bb.shape[0] != B:
             raise ValueError("bias needs one value per sequence")
         odt = torch.bfloat16 if out_dtype is None else out_dtype
+        if odt not in (torch.bfloat16, torch.float32):
+            raise ValueError("out_dtype must be bfloat16 or float32")
         if out is None:
             out = torch.empty_strided(q.shape, q.stride(), dtype=odt, device=q.device)
         if out.shape != q.shape or out.stride() != q.stride() or out.dtype != odt:
             raise ValueError("out must match q in shape and strides, with the output dtype")
-        code_dt = F32 if odt == torch.float32 else BF16
+        if out.device != q.device:
+            raise ValueError("out must be on q's GPU")
+        return bb, out, (F32 if odt == torch.float32 else BF16)
+
+    def decode(self, q, bias, *, scale=0.0, out=None, out_dtype=None, workspace=None):
+        """o[b, h] = sum over live entries of sigma(s q.k + beta_b [+ log(g+eps)]) [g] v.
+        bias: host sequence of B floats (beta_b). workspace: optional float32 device
+        tensor of at least workspace_size() bytes (allocated when omitted)."""
+        torch = _torch()
+        bb, out, code_dt = self._decode_args(q, bias, out, out_dtype)
+        lib = load()
         if workspace is None:
             workspace = torch.empty(max(1, (self.workspace_size() + 3) // 4),
                                     dtype=torch.float32, device=q.device)
+        if workspace.dtype != torch.float32 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous float32 tensor")
+        if workspace.device != q.device:
+            raise ValueError("workspace must be on q's GPU")
         code = lib.sigattn_decode(ctypes.byref(self.desc), q.data_ptr(), q.stride(0),
                                   q.stride(1), bb.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                                   float(scale), out.data_ptr(), code_dt, workspace.data_ptr(),
-                                  workspace.numel() * 4, _stream(q))
+                                  workspace.numel() * workspace.element_size(), _stream(q))
         _check(code, "sigattn_decode")
         return out
 
@@ -550,6 +576,8 @@ def _varlen_desc(q, k, tensors, cu_q, cu_k, max_q, max_k, causal, gate, tau, sin
             raise ValueError("cu_seqlens must be contiguous int32 tensors on q's GPU")
     if cu_q.numel() != cu_k.numel() or cu_q.numel() < 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k need B + 1 entries each")
+    if out_dtype is not None and out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bfloat16 or float32")
     for x in (gate, bias):
         if x is not None and (x.dtype != torch.float32 or x.device != q.device or not x.is_contiguous()):
             raise ValueError("gate and bias must be contiguous float32 tensors on q's GPU")
@@ -575,6 +603,28 @@ def _new_like(x, out_dtype):
     return torch.empty_strided(x.shape, x.stride(), dtype=dt, device=x.device)
 
 
+def _check_like(x, t, out_dtype, name):
+    """An output of a packed pass must match its input (q for o and dq, k for dk and dv)
+    in shape, strides and device, with the output dtype."""
+    torch = _torch()
+    dt = torch.bfloat16 if out_dtype is None else out_dtype
+    if (t.shape != x.shape or t.stride() != x.stride() or t.dtype != dt
+            or t.device != x.device):
+        raise ValueError(f"{name} must match its input in shape, strides and device, "
+                         f"with dtype {dt}")
+
+
+def _on_gpu(*tensors):
+    for t in tensors:
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("packed tensors must be on a GPU")
+
+
+def _same_shape(a, b, what):
+    if a.shape != b.shape:
+        raise ValueError(f"{what} must have the same shape")
+
+
 def fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, *, causal=False, gate=None, tau=0.0,
                sink=4, eps=1e-8, scale=0.0, bias=None, out=None, out_dtype=None,
                fast_math=False):
@@ -582,9 +632,12 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, *, causal=False, gate=None, ta
     device int32 [B + 1]; max_q, max_k host bounds on the sequence lengths; gate device
     float per key row; bias device float [B] (default -ln(nk))."""
     lib = load()
+    _same_shape(v, k, "v and k")
     p = _varlen_desc(q, k, (v,), cu_q, cu_k, max_q, max_k, causal, gate, tau, sink, eps, scale,
                      bias, out_dtype, fast_math)
     out = _new_like(q, out_dtype) if out is None else out
+    _check_like(q, out, out_dtype, "out")
+    _on_gpu(q, k, v, out, cu_q, cu_k, gate, bias)
     _check(lib.sigattn_fwd_varlen(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   out.data_ptr(), _stream(q)), "sigattn_fwd_varlen")
     return out
@@ -594,9 +647,13 @@ def bwd_dq_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k, *, causal=False, gate=N
                   sink=4, eps=1e-8, scale=0.0, bias=None, out=None, out_dtype=None,
                   fast_math=False):
     lib = load()
+    _same_shape(v, k, "v and k")
+    _same_shape(do, q, "do and q")
     p = _varlen_desc(q, k, (v, do), cu_q, cu_k, max_q, max_k, causal, gate, tau, sink, eps,
                      scale, bias, out_dtype, fast_math)
     out = _new_like(q, out_dtype) if out is None else out
+    _check_like(q, out, out_dtype, "dq")
+    _on_gpu(q, k, v, do, out, cu_q, cu_k, gate, bias)
     _check(lib.sigattn_bwd_dq_varlen(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      do.data_ptr(), out.data_ptr(), _stream(q)),
            "sigattn_bwd_dq_varlen")
@@ -607,9 +664,14 @@ def bwd_dkdv_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k, *, causal=False, gate
                     tau=0.0, sink=4, eps=1e-8, scale=0.0, bias=None, out=None, out_dtype=None,
                     fast_math=False):
     lib = load()
+    _same_shape(v, k, "v and k")
+    _same_shape(do, q, "do and q")
     p = _varlen_desc(q, k, (v, do), cu_q, cu_k, max_q, max_k, causal, gate, tau, sink, eps,
                      scale, bias, out_dtype, fast_math)
     dk, dv = (_new_like(k, out_dtype), _new_like(k, out_dtype)) if out is None else out
+    _check_like(k, dk, out_dtype, "dk")
+    _check_like(k, dv, out_dtype, "dv")
+    _on_gpu(q, k, v, do, dk, dv, cu_q, cu_k, gate, bias)
     _check(lib.sigattn_bwd_dkdv_varlen(ctypes.byref(p), q.data_ptr(), k.data_ptr(),
                                        v.data_ptr(), do.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                        _stream(q)), "sigattn_bwd_dkdv_varlen")
@@ -622,12 +684,18 @@ def bwd_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k, *, causal=False, gate=None
     """(dQ, dK, dV) of packed sequences in one call: the values of bwd_dq_varlen and
     bwd_dkdv_varlen, from one launch of both kernels at d = 64."""
     lib = load()
+    _same_shape(v, k, "v and k")
+    _same_shape(do, q, "do and q")
     p = _varlen_desc(q, k, (v, do), cu_q, cu_k, max_q, max_k, causal, gate, tau, sink, eps,
                      scale, bias, out_dtype, fast_math)
     if out is None:
         dq, dk, dv = _new_like(q, out_dtype), _new_like(k, out_dtype), _new_like(k, out_dtype)
     else:
         dq, dk, dv = out
+    _check_like(q, dq, out_dtype, "dq")
+    _check_like(k, dk, out_dtype, "dk")
+    _check_like(k, dv, out_dtype, "dv")
+    _on_gpu(q, k, v, do, dq, dk, dv, cu_q, cu_k, gate, bias)
     _check(lib.sigattn_bwd_varlen(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                   _stream(q)), "sigattn_bwd_varlen")

@@ -131,7 +131,9 @@ void fwd_kernel(const KArgs a) {
   // F16: P V runs on f16 operands where V allows. P is kept as 2^14 sigma (in [0, 2^14],
   // normal in f16 down to sigma = 2^-28) and rounded once to f16, 2^-11 relative, 8x
   // finer than bf16: one f16 product instead of the bf16 hi + lo pair. V's bf16 values
-  // are exact in f16 below 2^16 in magnitude; during tile t each thread converts its two
+  // with 2^-17 <= |v| < 2^16 are exact in f16; smaller ones fall into the f16 subnormals
+  // (absolute error at most 2^-25, zero below 2^-25), larger ones do not fit and flag
+  // the tile (below); during tile t each thread converts its two
   // 16-byte chunks of tile t+1's V in place and flags the tile if a value did not fit.
   // If any tile of the item was flagged, the workgroup computes the item again from the
   // start on bf16 hi + lo operands, with V loaded afresh and left unconverted. The tile

@@ -59,6 +59,31 @@ double scale_of(const sigattn_problem* p) {
 
 int tile_rows_d(int d, int pass);
 
+// Rows of d elements at offsets sum_i idx_i * stride_i (0 <= idx_i < count_i) must not
+// overlap, or outputs written through the shared strides would race. Sufficient test:
+// with the dimensions of count > 1 sorted by stride, each stride is at least the extent
+// of the dimensions below it (the first at least d).
+bool rows_disjoint(int64_t d, const int64_t* stride, const int64_t* count, int n) {
+  int64_t st[4], ct[4];
+  int m = 0;
+  for (int i = 0; i < n && m < 4; ++i)
+    if (count[i] > 1) { st[m] = stride[i]; ct[m] = count[i]; ++m; }
+  for (int i = 1; i < m; ++i)
+    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+      std::swap(st[j], st[j - 1]);
+      std::swap(ct[j], ct[j - 1]);
+    }
+  int64_t extent = d;   // elements spanned by the dimensions below
+  for (int i = 0; i < m; ++i) {
+    if (st[i] < extent) return false;
+    // extent of dims 0..i: the last row starts at (count-1)*stride (+ below), spans d more
+    const double e = (double)st[i] * (double)(ct[i] - 1) + (double)extent;
+    if (e > 9.0e18) return false;
+    extent = st[i] * (ct[i] - 1) + extent;
+  }
+  return true;
+}
+
 sigattn_status validate_problem(const sigattn_problem* p) {
   if (!p) return SIGATTN_ERR_INVALID_ARG;
   if (p->struct_size != sizeof(sigattn_problem)) return SIGATTN_ERR_INVALID_ARG;
@@ -92,6 +117,13 @@ sigattn_status validate_problem(const sigattn_problem* p) {
   const int64_t es = elem_size(p);
   if (((p->stride_l * es) & 15) || ((p->stride_h * es) & 15) || ((p->stride_b * es) & 15))
     return SIGATTN_ERR_ALIGNMENT;
+  // rows of different (batch entry, head, position) must not overlap: outputs share these
+  // strides
+  {
+    const int64_t stride[3] = {p->stride_b, p->stride_h, p->stride_l};
+    const int64_t count[3] = {p->B, p->H, p->Lmax};
+    if (!rows_disjoint(p->d, stride, count, 3)) return SIGATTN_ERR_INVALID_ARG;
+  }
   for (int pass = 0; pass < 3; ++pass) {
     const int tile = tile_rows_d(p->d, pass);
     int64_t items = 0;
@@ -289,6 +321,15 @@ sigattn_status validate_varlen(const sigattn_varlen* p) {
   if (p->stride_t < 0 || p->stride_h < 0) return SIGATTN_ERR_INVALID_ARG;
   if (p->stride_t > SIGATTN_MAX_ROW_STRIDE) return SIGATTN_ERR_UNSUPPORTED;
   if (((p->stride_t * 2) & 15) || ((p->stride_h * 2) & 15)) return SIGATTN_ERR_ALIGNMENT;
+  {
+    // packed rows of different (row, head) must not overlap; the row count is on the
+    // device, bounded by B times the larger of the two maximum lengths
+    const int64_t rows = (int64_t)p->B * (p->max_seqlen_q > p->max_seqlen_k ? p->max_seqlen_q
+                                                                             : p->max_seqlen_k);
+    const int64_t stride[2] = {p->stride_t, p->stride_h};
+    const int64_t count[2] = {rows > 2 ? rows : 2, p->H};
+    if (!rows_disjoint(p->d, stride, count, 2)) return SIGATTN_ERR_INVALID_ARG;
+  }
   if (!std::isfinite(p->scale) || p->scale < 0.0f) return SIGATTN_ERR_INVALID_ARG;
   if (p->B > 0 && (!p->cu_seqlens_q || !p->cu_seqlens_k)) return SIGATTN_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(p->cu_seqlens_q) & 3u) ||
@@ -410,6 +451,52 @@ int64_t decode_ws_bytes(const sigattn_cache* c) {
 // q/o rows ([B][H][d] with element strides sb, sh) must start on 16-byte boundaries
 bool rows16(int64_t sb, int64_t sh, int esize) {
   return sb >= 0 && sh >= 0 && ((sb * esize) & 15) == 0 && ((sh * esize) & 15) == 0;
+}
+
+// Single-query decode. internal_ws: the partial sums go to the library's static device
+// workspace (the allocation-free entry point) instead of the caller's `workspace`.
+sigattn_status decode_call(const sigattn_cache* c, const void* q, int64_t stride_b,
+                           int64_t stride_h, const float* bias, float scale, void* o,
+                           int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+                           void* stream, bool internal_ws) {
+  sigattn_status s = validate_cache(c);
+  if (s != SIGATTN_OK) return s;
+  if (out_dtype != SIGATTN_BF16 && out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || scale < 0.0f) return SIGATTN_ERR_INVALID_ARG;
+  if (c->B > 0 && !bias) return SIGATTN_ERR_INVALID_ARG;
+  for (int b = 0; b < c->B; ++b)
+    if (!std::isfinite(bias[b])) return SIGATTN_ERR_INVALID_ARG;
+  if (!q || !o || (!internal_ws && !workspace)) return SIGATTN_ERR_INVALID_ARG;
+  const int osize = out_dtype == SIGATTN_F32 ? 4 : 2;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(workspace) || !rows16(stride_b, stride_h, 2) ||
+      !rows16(stride_b, stride_h, osize))
+    return SIGATTN_ERR_ALIGNMENT;
+  if (stride_h < c->d && c->H > 1) return SIGATTN_ERR_INVALID_ARG;
+  if (!internal_ws && workspace_bytes < decode_ws_bytes(c)) return SIGATTN_ERR_INVALID_ARG;
+  const void* bufs[7] = {c->k, c->v, c->gate, c->count, c->seen, q, workspace};
+  for (int i = 0; i < 7; ++i) {
+    if (bufs[i] && bufs[i] == o) return SIGATTN_ERR_INVALID_ARG;
+    if (i < 6 && bufs[i] && bufs[i] == workspace) return SIGATTN_ERR_INVALID_ARG;
+  }
+  if (c->B == 0) return SIGATTN_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
+  if (internal_ws) return SIGATTN_ERR_UNSUPPORTED;
+  sa::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.c = cache_view(c);
+  a.q = q;
+  a.out = o;
+  a.ws = ws;
+  a.qsb = stride_b;
+  a.qsh = stride_h;
+  a.B = c->B;
+  a.nchunk = (int32_t)decode_chunks(c);
+  a.out_f32 = out_dtype == SIGATTN_F32 ? 1 : 0;
+  const double sc = scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)c->d);
+  a.c1 = (float)(-sc * kLog2eD);
+  for (int b = 0; b < c->B; ++b) a.c2[b] = (float)(-(double)bias[b] * kLog2eD);
+  return sa::launch_decode(a, st) == hipSuccess ? SIGATTN_OK : SIGATTN_ERR_HIP;
 }
 
 }  // namespace
@@ -631,42 +718,8 @@ sigattn_status sigattn_decode(const sigattn_cache* c, const void* q, int64_t str
                               int64_t stride_h, const float* bias, float scale, void* o,
                               int32_t out_dtype, void* workspace, int64_t workspace_bytes,
                               void* stream) {
-  sigattn_status s = validate_cache(c);
-  if (s != SIGATTN_OK) return s;
-  if (out_dtype != SIGATTN_BF16 && out_dtype != SIGATTN_F32) return SIGATTN_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || scale < 0.0f) return SIGATTN_ERR_INVALID_ARG;
-  if (c->B > 0 && !bias) return SIGATTN_ERR_INVALID_ARG;
-  for (int b = 0; b < c->B; ++b)
-    if (!std::isfinite(bias[b])) return SIGATTN_ERR_INVALID_ARG;
-  if (!q || !o || !workspace) return SIGATTN_ERR_INVALID_ARG;
-  const int osize = out_dtype == SIGATTN_F32 ? 4 : 2;
-  if (!aligned16(q) || !aligned16(o) || !aligned16(workspace) || !rows16(stride_b, stride_h, 2) ||
-      !rows16(stride_b, stride_h, osize))
-    return SIGATTN_ERR_ALIGNMENT;
-  if (stride_h < c->d && c->H > 1) return SIGATTN_ERR_INVALID_ARG;
-  if (workspace_bytes < decode_ws_bytes(c)) return SIGATTN_ERR_INVALID_ARG;
-  const void* bufs[7] = {c->k, c->v, c->gate, c->count, c->seen, q, workspace};
-  for (int i = 0; i < 7; ++i) {
-    if (bufs[i] && bufs[i] == o) return SIGATTN_ERR_INVALID_ARG;
-    if (i < 6 && bufs[i] && bufs[i] == workspace) return SIGATTN_ERR_INVALID_ARG;
-  }
-  if (c->B == 0) return SIGATTN_OK;
-  sa::DecodeArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.c = cache_view(c);
-  a.q = q;
-  a.out = o;
-  a.ws = static_cast<float*>(workspace);
-  a.qsb = stride_b;
-  a.qsh = stride_h;
-  a.B = c->B;
-  a.nchunk = (int32_t)decode_chunks(c);
-  a.out_f32 = out_dtype == SIGATTN_F32 ? 1 : 0;
-  const double sc = scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)c->d);
-  a.c1 = (float)(-sc * kLog2eD);
-  for (int b = 0; b < c->B; ++b) a.c2[b] = (float)(-(double)bias[b] * kLog2eD);
-  return sa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
-             ? SIGATTN_OK : SIGATTN_ERR_HIP;
+  return decode_call(c, q, stride_b, stride_h, bias, scale, o, out_dtype, workspace,
+                     workspace_bytes, stream, false);
 }
 
 int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int64_t cap,

@@ -339,9 +339,14 @@ def _varlen(**kw):
     (lambda p: setattr(p, "cu_seqlens_k", (1 << 20) + 2), 3),
     (lambda p: setattr(p, "scale", -2.0), 1),
     (lambda p: (setattr(p, "gate", 1 << 24), setattr(p, "gate_tau", -1.0)), 1),
-    (lambda p: (setattr(p, "B", 1 << 20), setattr(p, "H", 64), setattr(p, "max_seqlen_k", 1 << 20)), 2),
+    (lambda p: (setattr(p, "B", 1 << 20), setattr(p, "H", 64), setattr(p, "stride_t", 64 * 64),
+                setattr(p, "max_seqlen_k", 1 << 20)), 2),
     # B * H * ceil(max rows / 128) one past the work-item cap (2^23 - 1)
-    (lambda p: (setattr(p, "B", 1 << 16), setattr(p, "H", 128), setattr(p, "max_seqlen_q", 100)), 2),
+    (lambda p: (setattr(p, "B", 1 << 16), setattr(p, "H", 128), setattr(p, "stride_t", 128 * 64),
+                setattr(p, "max_seqlen_q", 100)), 2),
+    # rows of different heads overlap: stride_h below d, or heads wider than the row stride
+    (lambda p: setattr(p, "stride_h", 32), 1),
+    (lambda p: setattr(p, "H", 3), 1),
     (lambda p: setattr(p, "struct_size", 8), 1),
 ])
 def test_varlen_validation_before_launch(lib, mutate, code):
@@ -374,3 +379,4 @@ def test_varlen_output_checks(lib):
     assert lib.sigattn_bwd_varlen(ctypes.byref(p), q, k, v, q, None, three, four, None) == 1
     assert lib.sigattn_bwd_varlen(ctypes.byref(p), q, k, v, q, vp((1 << 25) + 8), three, four,
                                   None) == 3
+

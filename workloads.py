@@ -48,7 +48,7 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "generate", "generate_decode", "round_to_bf16",
-           "valid_pairs", "flops_forward", "flops_backward"]
+           "seqlens_of", "valid_pairs", "flops_forward", "flops_backward"]
 
 
 @dataclass(frozen=True)
@@ -144,6 +144,14 @@ def _lengths(w: Workload, rng) -> np.ndarray:
     else:
         raise ValueError(kind)
     return np.clip(n, 0, w.L).astype(np.int32)
+
+
+def seqlens_of(w: Workload | str) -> np.ndarray:
+    """The valid lengths of a workload: the first draw of ``generate`` (same seed, so the
+    same lengths)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    return _lengths(w, np.random.default_rng(w.seed))
 
 
 def generate(w: Workload | str, poison: bool = False, with_do: bool = True) -> dict:
