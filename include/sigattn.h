@@ -47,7 +47,8 @@
  *  - seqlens and bias are HOST arrays of length B, read during the call only.
  *    gate is a DEVICE array of floats, gate[b * gate_stride_b + j], j < Lmax.
  *  - The caller owns every buffer. The library never allocates, frees or
- *    synchronises; only sigattn_decode needs a workspace, which the caller passes.
+ *    synchronises; only sigattn_decode needs a workspace, which the caller passes
+ *    (sigattn_decode_noalloc uses a static device array of the library instead).
  *    Work is enqueued on `stream` (a hipStream_t; NULL is the default stream) and the
  *    results are valid once that stream has completed it. Identical inputs give
  *    bitwise-identical outputs (no atomics).
@@ -292,6 +293,23 @@ sigattn_status sigattn_decode(const sigattn_cache* c, const void* q, int64_t str
                               int64_t stride_h, const float* bias, float scale, void* o,
                               int32_t out_dtype, void* workspace, int64_t workspace_bytes,
                               void* stream);
+
+/* Single-query decode that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory or call hipMalloc (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same arguments, results and errors
+ * as sigattn_decode without workspace and workspace_bytes; the per-chunk partial sums go
+ * to a static device array inside the library instead, SIGATTN_NOALLOC_WORKSPACE_BYTES
+ * (16 MiB) on every GPU the library runs on, held until the process ends. A cache whose
+ * sigattn_decode_workspace_size exceeds that limit returns SIGATTN_ERR_UNSUPPORTED and
+ * nothing is enqueued. Every call on one GPU shares that GPU's array and leaves the last
+ * call's partial sums in it (each call writes the entries it reads before reading them):
+ * calls that overlap in time on one GPU (different streams, or different host threads
+ * without ordering) race and give undefined results. The first call on each device looks
+ * up the array's device address (hipGetSymbolAddress); later calls reuse it. */
+#define SIGATTN_NOALLOC_WORKSPACE_BYTES (16LL << 20)
+sigattn_status sigattn_decode_noalloc(const sigattn_cache* c, const void* q, int64_t stride_b,
+                                      int64_t stride_h, const float* bias, float scale, void* o,
+                                      int32_t out_dtype, void* stream);
 
 /* Host-side view of the work list a pass launches, for inspection and tests.
  * pass: 0 forward, 1 dq, 2 dk/dv. Writes up to `cap` items as (b, h, tile) int32

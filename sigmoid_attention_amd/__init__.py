@@ -16,6 +16,7 @@ raises, there is no fallback.
     dq, dk, dv = bwd_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k)
     cache = KVCache(B, H, d, cap, gated=True, tau=0.05)   # KV cache with eviction
     cache.build(k, v, seqlens, gate=g); cache.append(k1, v1, g1); o1 = cache.decode(q1, bias)
+    o1 = cache.decode_noalloc(q1, bias, out=o1)              # no workspace, no allocation
 
 Tensors are [B, H, Lmax, d] views (any strides with a contiguous last dimension, the
 same strides for all of them), bf16 or float32 (the float32 debug path), on one GPU.
@@ -33,7 +34,7 @@ import numpy as np
 __all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd", "bwd_dkdv_dg", "fwd_varlen",
            "bwd_dq_varlen", "bwd_dkdv_varlen", "bwd_varlen", "VarlenDesc", "KVCache",
            "CacheDesc", "validate", "plan", "calibrate_mfma", "library_path", "load",
-           "Problem", "SigattnError", "STATUS", "VERSION"]
+           "Problem", "SigattnError", "STATUS", "VERSION", "NOALLOC_WORKSPACE_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsigattn.so")
@@ -42,6 +43,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem",
           3: "misaligned pointer or stride", 4: "HIP runtime error"}
 BF16, F32 = 0, 1
 VERSION = 2
+NOALLOC_WORKSPACE_BYTES = 16 << 20   # static decode workspace of sigattn_decode_noalloc
 
 
 class SigattnError(RuntimeError):
@@ -170,7 +172,10 @@ def load():
     lib.sigattn_decode_workspace_size.restype = i64
     lib.sigattn_decode.argtypes = [C, vp, i64, i64, ctypes.POINTER(ctypes.c_float), ctypes.c_float,
                                    vp, ctypes.c_int32, vp, i64, vp]
-    for f in (lib.sigattn_cache_build, lib.sigattn_cache_append, lib.sigattn_decode):
+    lib.sigattn_decode_noalloc.argtypes = [C, vp, i64, i64, ctypes.POINTER(ctypes.c_float),
+                                           ctypes.c_float, vp, ctypes.c_int32, vp]
+    for f in (lib.sigattn_cache_build, lib.sigattn_cache_append, lib.sigattn_decode,
+              lib.sigattn_decode_noalloc):
         f.restype = ctypes.c_int
     lib.sigattn_plan.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                  ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]
@@ -558,6 +563,18 @@ class KVCache:
                                   float(scale), out.data_ptr(), code_dt, workspace.data_ptr(),
                                   workspace.numel() * workspace.element_size(), _stream(q))
         _check(code, "sigattn_decode")
+        return out
+
+    def decode_noalloc(self, q, bias, *, scale=0.0, out=None, out_dtype=None):
+        """decode() through sigattn_decode_noalloc: no workspace, the library's static
+        device array holds the partial sums (the cache's workspace_size() must not exceed
+        16 MiB). With `out` given, nothing is allocated."""
+        bb, out, code_dt = self._decode_args(q, bias, out, out_dtype)
+        code = load().sigattn_decode_noalloc(
+            ctypes.byref(self.desc), q.data_ptr(), q.stride(0), q.stride(1),
+            bb.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), float(scale), out.data_ptr(),
+            code_dt, _stream(q))
+        _check(code, "sigattn_decode_noalloc")
         return out
 
 

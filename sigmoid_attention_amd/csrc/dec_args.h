@@ -9,6 +9,8 @@ namespace sa {
 
 constexpr int kDecChunk = 512;   // cache entries per decode workgroup
 constexpr int kBuildRows = 256;  // prefill rows per cache-build workgroup
+// floats of the static device workspace of the allocation-free decode (16 MiB per GPU)
+constexpr int64_t kNoAllocFloats = int64_t(1) << 22;
 
 struct CacheView {
   void* k;               // [B][H][cap][d] bf16

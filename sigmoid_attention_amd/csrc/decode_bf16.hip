@@ -25,10 +25,49 @@
 //    workspace and added up in chunk order by a second kernel: deterministic, no atomics.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "dec_args.h"
 
 namespace sa {
+
+// Workspace of the allocation-free decode entry point: the per-chunk partial sums live in
+// this file-scope device array instead of caller memory. Each GPU the library runs on
+// holds its own copy until the process ends. In host code the name `scratch` is only a
+// host-side stand-in: its device address is looked up per device (noalloc_scratch) and
+// only that address is ever handed to a kernel.
+static __device__ __align__(256) float scratch[kNoAllocFloats];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the device that `stream` belongs to, looked up once per
+// device with that device current (hipGetSymbolAddress), then cached.
+hipError_t noalloc_scratch(hipStream_t stream, float** out) {
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 // ------------------------------------ cache build ------------------------------------
 

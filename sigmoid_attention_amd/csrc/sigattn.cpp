@@ -32,6 +32,7 @@ hipError_t launch_f32(const DArgs& a, int pass, hipStream_t st);
 hipError_t launch_cache_build(const BuildArgs& a, int B, hipStream_t st);
 hipError_t launch_cache_append(const AppendArgs& a, int B, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t noalloc_scratch(hipStream_t stream, float** out);
 int calib_mfma_per_iter();
 hipError_t launch_mfma_calib(float* sink, int64_t* clk, int nblocks, int iters, hipStream_t st);
 }  // namespace sa
@@ -41,6 +42,9 @@ namespace {
 using sa::KArgs;
 
 constexpr double kLog2eD = 1.4426950408889634;
+
+static_assert(SIGATTN_NOALLOC_WORKSPACE_BYTES == sa::kNoAllocFloats * (int64_t)sizeof(float),
+              "the header's limit must match the static workspace");
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -472,7 +476,11 @@ sigattn_status decode_call(const sigattn_cache* c, const void* q, int64_t stride
       !rows16(stride_b, stride_h, osize))
     return SIGATTN_ERR_ALIGNMENT;
   if (stride_h < c->d && c->H > 1) return SIGATTN_ERR_INVALID_ARG;
-  if (!internal_ws && workspace_bytes < decode_ws_bytes(c)) return SIGATTN_ERR_INVALID_ARG;
+  if (internal_ws) {
+    if (decode_ws_bytes(c) > SIGATTN_NOALLOC_WORKSPACE_BYTES) return SIGATTN_ERR_UNSUPPORTED;
+  } else if (workspace_bytes < decode_ws_bytes(c)) {
+    return SIGATTN_ERR_INVALID_ARG;
+  }
   const void* bufs[7] = {c->k, c->v, c->gate, c->count, c->seen, q, workspace};
   for (int i = 0; i < 7; ++i) {
     if (bufs[i] && bufs[i] == o) return SIGATTN_ERR_INVALID_ARG;
@@ -481,7 +489,7 @@ sigattn_status decode_call(const sigattn_cache* c, const void* q, int64_t stride
   if (c->B == 0) return SIGATTN_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* ws = static_cast<float*>(workspace);
-  if (internal_ws) return SIGATTN_ERR_UNSUPPORTED;
+  if (internal_ws && sa::noalloc_scratch(st, &ws) != hipSuccess) return SIGATTN_ERR_HIP;
   sa::DecodeArgs a;
   std::memset(&a, 0, sizeof(a));
   a.c = cache_view(c);
@@ -720,6 +728,13 @@ sigattn_status sigattn_decode(const sigattn_cache* c, const void* q, int64_t str
                               void* stream) {
   return decode_call(c, q, stride_b, stride_h, bias, scale, o, out_dtype, workspace,
                      workspace_bytes, stream, false);
+}
+
+sigattn_status sigattn_decode_noalloc(const sigattn_cache* c, const void* q, int64_t stride_b,
+                                      int64_t stride_h, const float* bias, float scale, void* o,
+                                      int32_t out_dtype, void* stream) {
+  return decode_call(c, q, stride_b, stride_h, bias, scale, o, out_dtype, nullptr, 0, stream,
+                     true);
 }
 
 int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int64_t cap,

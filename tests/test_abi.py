@@ -380,3 +380,27 @@ def test_varlen_output_checks(lib):
     assert lib.sigattn_bwd_varlen(ctypes.byref(p), q, k, v, q, vp((1 << 25) + 8), three, four,
                                   None) == 3
 
+
+def test_noalloc_decode_checks_before_launch(lib):
+    """sigattn_decode_noalloc validates like sigattn_decode and refuses a cache whose
+    partial sums would not fit the library's 16 MiB static workspace; nothing is enqueued
+    (fake device pointers)."""
+    vp = ctypes.c_void_p
+    q, o = vp(1 << 24), vp(1 << 25)
+    f = lib.sigattn_decode_noalloc
+    c = _cache()
+    bias = (ctypes.c_float * 2)(-1.0, -2.0)
+    assert f(ctypes.byref(c), q, 3 * 64, 64, None, 0.0, o, 0, None) == 1       # no bias
+    assert f(ctypes.byref(c), q, 3 * 64, 64, bias, 0.0, q, 0, None) == 1       # o aliases q
+    assert f(ctypes.byref(c), vp((1 << 24) + 4), 3 * 64, 64, bias, 0.0, o, 0, None) == 3
+    assert f(ctypes.byref(c), q, 3 * 64, 64, bias, 0.0, o, 7, None) == 2
+    # B * H * ceil(cap / 512) * d floats: 32 * 16 * 70 * 128 * 4 bytes > 16 MiB
+    big = _cache(B=32, H=16, d=128, cap=70 * 512, stride_b=16 * 70 * 512 * 128,
+                 stride_h=70 * 512 * 128, stride_l=128)
+    assert lib.sigattn_decode_workspace_size(ctypes.byref(big)) > S.NOALLOC_WORKSPACE_BYTES
+    b32 = (ctypes.c_float * 32)(*([-1.0] * 32))
+    assert f(ctypes.byref(big), q, 16 * 128, 128, b32, 0.0, o, 0, None) == 2
+    # one chunk fewer per (sequence, head) fits exactly: 32 * 16 * 64 * 128 * 4 = 16 MiB
+    fits = _cache(B=32, H=16, d=128, cap=64 * 512, stride_b=16 * 64 * 512 * 128,
+                  stride_h=64 * 512 * 128, stride_l=128)
+    assert lib.sigattn_decode_workspace_size(ctypes.byref(fits)) == S.NOALLOC_WORKSPACE_BYTES
