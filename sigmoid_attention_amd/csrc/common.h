@@ -245,6 +245,71 @@ struct DirectTile {
   }
 };
 
+// Direct loads of one ring stage holding two tiles with the same layout and strides (K
+// and V, or Q and dO), the second TILE bytes after the first. A tile whose rows are all
+// valid takes the fast path: this wave's two 1 KB blocks of a tile sit NWAVES blocks
+// apart, and the swizzle depends on the low four row bits only, which the two blocks
+// share, so one per-lane offset (computed once) serves every interior tile and both
+// blocks: the second block's source is the first's plus a fixed number of rows. Per tile
+// the fast path issues four loads with no vector arithmetic and one wait for SGPRs
+// written by vector instructions per tensor. Edge tiles clamp rows to the last valid row
+// (DirectTile).
+// A wave-uniform 64-bit value in scalar registers (readfirstlane returns int: go through
+// uint32_t so that the low half is not sign-extended)
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+template <int ROWS, int D, int NWAVES>
+struct DirectPair {
+  using Tile = DirectTile<ROWS, D, NWAVES>;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = ROWS * D * 2;
+  static constexpr int ROWS_APART = NWAVES * 64 / CPR;   // rows between this wave's blocks
+  static_assert(Tile::PER_WAVE == 2, "two blocks per wave and tile");
+  static_assert(ROWS_APART % 16 == 0, "the two blocks must share the low four row bits");
+  uint32_t voff;       // per-lane byte offset of block 0 within an interior tile
+  uint32_t rb;         // row stride in bytes
+  int w;               // wave index (uniform)
+
+  __device__ __forceinline__ DirectPair(int64_t sl) {
+    const int l = lane_id();
+    w = __builtin_amdgcn_readfirstlane(wave_id());
+    rb = (uint32_t)sl * 2u;
+    const int P = w * 64 + l;
+    const int row = P / CPR;
+    voff = (uint32_t)row * rb + (uint32_t)(((P % CPR) ^ xsw<D>(row)) * 16);
+  }
+
+  __device__ __forceinline__ void fast(const char* base, uint32_t lds) const {
+    const uint64_t b0 = uniform_u64(reinterpret_cast<uintptr_t>(base));
+    const uint64_t b1 = uniform_u64(b0 + (uint64_t)ROWS_APART * rb);
+    const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds);
+    const uint32_t lds1 = (uint32_t)__builtin_amdgcn_readfirstlane(lds + (uint32_t)NWAVES * 1024u);
+    // 5 wait states between a vector write of an SGPR operand and the memory instruction
+    // reading it (once for both loads), 1 between the SALU write of M0 and the LDS DMA
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %3\n\t"
+                 "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4"
+                 :: "v"(voff), "s"(lds0), "s"(lds1), "s"(b0), "s"(b1) : "memory");
+  }
+
+  // rows row_base .. row_base + ROWS - 1 of a and b into the stage at lds_stage
+  __device__ __forceinline__ void load(char* lds_stage, const bf16* a, const bf16* b, int64_t sl,
+                                       int row_base, int last_row) const {
+    if (row_base + ROWS - 1 <= last_row) {
+      const uint32_t lds = (uint32_t)(uintptr_t)(SA_LDS char*)lds_stage + (uint32_t)w * 1024u;
+      const int64_t off = (int64_t)row_base * sl;
+      fast(reinterpret_cast<const char*>(a + off), lds);
+      fast(reinterpret_cast<const char*>(b + off), lds + (uint32_t)TILE);
+    } else {
+      Tile::load(lds_stage, a, sl, row_base, last_row);
+      Tile::load(lds_stage + TILE, b, sl, row_base, last_row);
+    }
+  }
+};
+
 // The work item of this workgroup, with every field made explicitly wave-uniform (scalar
 // registers), so that the tensor base pointers derived from it stay in scalar registers.
 // Packed mode: the item's sequence bounds come from the device arrays cu_q / cu_k.

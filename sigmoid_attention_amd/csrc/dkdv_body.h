@@ -54,7 +54,6 @@ template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool DG, bool VL>
 __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* smem,
                                           void* out_k, void* out_v) {
   using T = DkvTraits<D, CPT>;
-  using Tile = DirectTile<T::BQ, D, T::kWaves>;
   constexpr bool PIPE = D == 64;
 
   const int l = lane_id(), w = wave_id();
@@ -96,10 +95,9 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
   // loaded first, else at the start of that unit (a causal shift can put it later)
   const bool s_late = VL && CAUSAL && PIPE && c_lo < nch && c_lo / CPT > t0 + 1;
 
+  const DirectPair<T::BQ, D, T::kWaves> dma(sl);
   auto issue_tile = [&](int t) {
-    char* st = smem + (t % T::NSTAGE) * T::STAGE;
-    Tile::load(st, Qg, sl, t * T::BQ, lastq);
-    Tile::load(st + T::TILE, dOg, sl, t * T::BQ, lastq);
+    dma.load(smem + (t % T::NSTAGE) * T::STAGE, Qg, dOg, sl, t * T::BQ, lastq);
   };
   if (t0 < ntiles) issue_tile(t0);
   if (t0 + 1 < ntiles) issue_tile(t0 + 1);

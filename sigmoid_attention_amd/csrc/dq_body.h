@@ -45,7 +45,6 @@ __device__ __forceinline__ constexpr int dq_arc(int r) { return 8 * (r >> 2) + (
 template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool VL>
 __device__ __forceinline__ void dq_body(const KArgs& a, const Item& it, char* smem, void* out) {
   using T = DqTraits<D, CPT, GATED>;
-  using Tile = DirectTile<T::BN, D, T::kWaves>;
 
   const int l = lane_id(), w = wave_id();
   const int lk = 4 * (l >> 5);
@@ -76,10 +75,9 @@ __device__ __forceinline__ void dq_body(const KArgs& a, const Item& it, char* sm
     wch = lk_allowed < 0 ? 0 : (lk_allowed / 32 + 1 < nch ? lk_allowed / 32 + 1 : nch);
   }
 
+  const DirectPair<T::BN, D, T::kWaves> dma(sl);
   auto issue_tile = [&](int t) {
-    char* st = smem + (t % T::NSTAGE) * T::STAGE;
-    Tile::load(st, Kg, sl, t * T::BN, lastk);
-    Tile::load(st + T::TILE, Vg, sl, t * T::BN, lastk);
+    dma.load(smem + (t % T::NSTAGE) * T::STAGE, Kg, Vg, sl, t * T::BN, lastk);
   };
   auto fill_table = [&](int t) {
     if (GATED && w == 0 && l < T::BN) {

@@ -68,7 +68,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<D, Q
 void fwd_kernel(const KArgs a) {
   static_assert(SPLIT || !F16, "f16 operands replace the hi + lo split");
   using T = FwdTraits<D, QB, CPT, GATED>;
-  using Tile = DirectTile<T::BN, D, T::kWaves>;
   __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
   // F16: per ring slot, set when some value of that tile's V does not fit f16
   __shared__ int vflag[T::NSTAGE];
@@ -111,10 +110,9 @@ void fwd_kernel(const KArgs a) {
     wch = lk_allowed < 0 ? 0 : (lk_allowed / 32 + 1 < nch ? lk_allowed / 32 + 1 : nch);
   }
 
+  const DirectPair<T::BN, D, T::kWaves> dma(sl);
   auto issue_tile = [&](int t) {
-    char* st = smem + (t % T::NSTAGE) * T::STAGE;
-    Tile::load(st, Kg, sl, t * T::BN, lastk);
-    Tile::load(st + T::TILE, Vg, sl, t * T::BN, lastk);
+    dma.load(smem + (t % T::NSTAGE) * T::STAGE, Kg, Vg, sl, t * T::BN, lastk);
   };
   // gate table of tile t: logit offset in the exp2 domain (+inf drops the key, which
   // gives P = 0 exactly) and value factor, one entry per key, written by wave 0
