@@ -18,6 +18,7 @@ Two checks are used.
   (|delta sigma'| <= 2^-23).
 """
 
+import functools
 import sys
 
 import numpy as np
@@ -80,6 +81,13 @@ def oracle_kwargs(data):
     g = None if data["gate"] is None else data["gate"].astype(np.float64)
     return dict(causal=bool(data["causal"]), gate=g, tau=float(data["tau"]),
                 sink=int(data["sink"]))
+
+
+@functools.lru_cache(maxsize=1)
+def oracle_full_named(name):
+    """oracle_full of a named workload's seeded inputs, kept for the next caller."""
+    import workloads as W
+    return oracle_full(W.generate(name))
 
 
 def oracle_full(data):

@@ -11,7 +11,8 @@ import pytest
 import oracle as O
 import workloads as W
 from gpu_util import (BF16_TOL, F32_TOL, bound_excess, check_all, check_bounds, err_ratio,
-                      need_gpu, note, oracle_full, oracle_kwargs, oracle_magnitudes, run_gpu)
+                      need_gpu, note, oracle_full, oracle_full_named, oracle_kwargs,
+                      oracle_magnitudes, run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,7 +122,8 @@ def _sample_rows(n, L, rng, tile=64):
                                   "sweep_16k_d64_p25", "sweep_16k_d128", "sweep_512_d128_p25"])
 def test_full_size_sampled(name):
     """Full-size workloads in the launch configuration the benchmark times, checked on
-    sampled rows that the oracle computes one by one."""
+    sampled rows (first and last, tile edges, random) of the first and last head of every
+    batch entry, which the oracle computes one by one."""
     torch = need_gpu()
     data = W.generate(name)
     note(f"{name} full size: fwd, dq, dkdv, float outputs")
@@ -132,8 +134,8 @@ def test_full_size_sampled(name):
     sl = data["seqlens"]
     B, H, L, d = data["q"].shape
     rng = np.random.default_rng(5)
-    order = np.argsort(sl)
-    picks = {(int(order[0]), 0), (int(order[-1]), H - 1), (int(rng.integers(B)), int(rng.integers(H)))}
+    # every batch entry, its first and last head
+    picks = {(b, h) for b in range(B) if sl[b] > 0 for h in (0, H - 1)}
     refs = {"O": [], "dQ": [], "dK": [], "dV": []}
     gots = {"O": [], "dQ": [], "dK": [], "dV": []}
     fasts = {"O": [], "dQ": [], "dK": [], "dV": []}
@@ -176,6 +178,17 @@ def test_full_size_sampled(name):
         for key in ("O", "dQ", "dK", "dV"):
             assert np.all(np.isfinite(out[key][mask]))
             assert np.all(out[key][~mask] == 0.0)
+
+
+def test_bidir_2k_full():
+    """The 2K bidirectional batch (B=8, H=16, d=64, n ~ U{1024..2048}) compared element
+    by element with the full fp64 oracle: every valid row of O, dQ, dK, dV of every head
+    at the stated bar, padded rows exactly 0."""
+    torch = need_gpu()
+    data = W.generate("bidir_2k")
+    note("bidir_2k full comparison, float outputs")
+    gpu = run_gpu(data, torch.bfloat16, out_dtype=torch.float32)
+    print(check_all(gpu, oracle_full_named("bidir_2k"), data["seqlens"], BF16_TOL, "bidir_2k full"))
 
 
 @pytest.mark.parametrize("causal", [False, True])
