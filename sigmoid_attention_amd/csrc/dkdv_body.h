@@ -179,13 +179,14 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
   //   3: bf16 of h = 1                        | dV, dK for the first query half of c
   //   4: -                                    | dV, dK for the second query half
   // (the MFMA-only step overlaps the VALU steps of the other wave on the SIMD)
+  const LdsLane<D> lane;
   auto unit = [&](auto mode_tag, const char* Qc, const char* dOc, int qrow, const char* Qn,
                   int qn_row, int qb0) {
     bf16x8 dor[T::KS], qnr[T::KS];
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) dor[ks] = lds_row_operand<D>(dOc, qrow, 16 * ks);
+    for (int ks = 0; ks < T::KS; ++ks) dor[ks] = lane.rowop(dOc, qrow, ks);
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) qnr[ks] = lds_row_operand<D>(Qn, qn_row, 16 * ks);
+    for (int ks = 0; ks < T::KS; ++ks) qnr[ks] = lane.rowop(Qn, qn_row, ks);
     __builtin_amdgcn_sched_barrier(0);
     // step 1
     f32x16 p, dp = zero16(), s_next = zero16();
@@ -199,8 +200,8 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
     bf16x8 do0[T::DT], qc0[T::DT];
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) {
-      do0[dt] = lds_col_operand<D>(dOc, qrow, 32 * dt);
-      qc0[dt] = lds_col_operand<D>(Qc, qrow, 32 * dt);
+      do0[dt] = lane.colop(dOc, qrow, dt);
+      qc0[dt] = lane.colop(Qc, qrow, dt);
     }
     f32x16 ds;
 #pragma unroll
@@ -214,8 +215,8 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
     bf16x8 do1[T::DT], qc1[T::DT];
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) {
-      do1[dt] = lds_col_operand<D>(dOc, qrow + 16, 32 * dt);
-      qc1[dt] = lds_col_operand<D>(Qc, qrow + 16, 32 * dt);
+      do1[dt] = lane.colop(dOc, qrow + 16, dt);
+      qc1[dt] = lane.colop(Qc, qrow + 16, dt);
     }
     to_bf16(p, 1, ph1, pl1);
     to_bf16(ds, 1, dh1, dl1);
@@ -277,12 +278,17 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
   tm2 = tm2 > tm1 ? tm2 : tm1;
   tm2 = tm2 < ntiles ? tm2 : ntiles;
 
-  auto tile_body = [&](auto mode_tag, int t) {
+  // `stage_tag`: the ring slot of tile t, a compile-time constant in the unrolled interior
+  // loop (LDS addresses fold into immediate offsets), or -1 when computed
+  auto tile_body = [&](auto mode_tag, auto stage_tag, int t) {
     constexpr int MODE = decltype(mode_tag)::value;
+    constexpr int SG = decltype(stage_tag)::value;
     if (t > t0) wait_vmem_and_barrier();
     if (t + 2 < ntiles) issue_tile(t + 2);
-    const char* cur = smem + (t % T::NSTAGE) * T::STAGE;
-    const char* nxt = smem + ((t + 1) % T::NSTAGE) * T::STAGE;
+    const int st = SG >= 0 ? SG : t % T::NSTAGE;
+    const int st1 = SG >= 0 ? (SG + 1) % T::NSTAGE : (t + 1) % T::NSTAGE;
+    const char* cur = smem + st * T::STAGE;
+    const char* nxt = smem + st1 * T::STAGE;
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
       const int c = t * CPT + cc;
@@ -302,9 +308,25 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
       }
     }
   };
-  for (int t = t0; t < tm1; ++t) tile_body(std::integral_constant<int, kKvMasked>{}, t);
-  for (int t = tm1; t < tm2; ++t) tile_body(std::integral_constant<int, kKvInterior>{}, t);
-  for (int t = tm2; t < ntiles; ++t) tile_body(std::integral_constant<int, kKvMasked>{}, t);
+  using Msk = std::integral_constant<int, kKvMasked>;
+  using Int = std::integral_constant<int, kKvInterior>;
+  using Dyn = std::integral_constant<int, -1>;
+  for (int t = t0; t < tm1; ++t) tile_body(Msk{}, Dyn{}, t);
+  {
+    // interior tiles: up to a multiple of the ring size one at a time, then whole turns
+    // of the ring with compile-time slots
+    int t = tm1;
+    for (; t < tm2 && t % T::NSTAGE != 0; ++t) tile_body(Int{}, Dyn{}, t);
+    if (PIPE) {
+      for (; t + 3 <= tm2; t += 3) {
+        tile_body(Int{}, std::integral_constant<int, 0>{}, t);
+        tile_body(Int{}, std::integral_constant<int, 1>{}, t + 1);
+        tile_body(Int{}, std::integral_constant<int, 2>{}, t + 2);
+      }
+    }
+    for (; t < tm2; ++t) tile_body(Int{}, Dyn{}, t);
+  }
+  for (int t = tm2; t < ntiles; ++t) tile_body(Msk{}, Dyn{}, t);
 
   if (DG) {
     // v_j . (sum_i P_ij dO_i): this lane holds features 32 dt + 8 m + lk + e of the dV
