@@ -79,20 +79,28 @@ __device__ __forceinline__ void dq_body(const KArgs& a, const Item& it, char* sm
   auto issue_tile = [&](int t) {
     dma.load(smem + (t % T::NSTAGE) * T::STAGE, Kg, Vg, sl, t * T::BN, lastk);
   };
-  auto fill_table = [&](int t) {
-    if (GATED && w == 0 && l < T::BN) {
+  // gate table of tile t (as in the forward), written by wave 0 from gate values read
+  // one tile ahead, so that the wait for them does not also wait for the direct loads
+  const bool gate_lane = GATED && w == 0 && l < T::BN;
+  auto gate_value = [&](int t) {
+    const int key = t * T::BN + l;
+    return Gg[key < lastk ? key : lastk];
+  };
+  auto store_table = [&](int t, float g) {
+    if (gate_lane) {
       float* tab = reinterpret_cast<float*>(smem + (t % T::NSTAGE) * T::STAGE + 2 * T::TILE);
       const int key = t * T::BN + l;
-      const float g = Gg[key < lastk ? key : lastk];
       const bool keep = key < nk && !(key >= a.gate_sink && g < a.gate_tau);
       tab[l] = keep ? c2 - __builtin_amdgcn_logf(g + a.gate_eps) : __builtin_inff();
       tab[T::BN + l] = keep ? g : 0.0f;
     }
   };
-  if (ntiles > 0) {
-    issue_tile(0);
-    fill_table(0);
-  }
+  // gate values for the tables of tiles 0 and t + 1; the table of tile 0 is written once
+  // the loads issued after them are awaited, before the barrier that publishes the tile
+  float gfirst = 0.0f, gnext = 0.0f;
+  if (gate_lane && ntiles > 0) gfirst = gate_value(0);
+  if (gate_lane && ntiles > 1) gnext = gate_value(1);
+  if (ntiles > 0) issue_tile(0);
   if (ntiles > 1) issue_tile(1);
 
   bf16x8 qop[T::KS], doop[T::KS];
@@ -117,6 +125,7 @@ __device__ __forceinline__ void dq_body(const KArgs& a, const Item& it, char* sm
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) acc[dt] = zero16();
 
+  if (ntiles > 0) store_table(0, gfirst);
   wait_vmem_and_barrier();
 
   // S^T and dP^T of chunk 0
@@ -254,8 +263,12 @@ __device__ __forceinline__ void dq_body(const KArgs& a, const Item& it, char* sm
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr int SG = decltype(stage_tag)::value;
     if (t > 0) wait_vmem_and_barrier();
-    if (t + 2 < ntiles) issue_tile(t + 2);
-    if (t + 1 < ntiles) fill_table(t + 1);
+    // gnext was read during the previous tile (or before the first) and has arrived
+    if (t + 1 < ntiles) store_table(t + 1, gnext);
+    if (t + 2 < ntiles) {
+      if (gate_lane) gnext = gate_value(t + 2);
+      issue_tile(t + 2);
+    }
     const int st = SG >= 0 ? SG : t % T::NSTAGE;
     const int st1 = SG >= 0 ? (SG + 1) % T::NSTAGE : (t + 1) % T::NSTAGE;
     const char* cur = smem + st * T::STAGE;

@@ -115,16 +115,33 @@ void fwd_kernel(const KArgs a) {
     dma.load(smem + (t % T::NSTAGE) * T::STAGE, Kg, Vg, sl, t * T::BN, lastk);
   };
   // gate table of tile t: logit offset in the exp2 domain (+inf drops the key, which
-  // gives P = 0 exactly) and value factor, one entry per key, written by wave 0
-  auto fill_table = [&](int t) {
-    if (GATED && w == 0 && l < T::BN) {
+  // gives P = 0 exactly) and value factor, one entry per key, written by wave 0 (lanes
+  // below BN) from the gate value g of its key. The values are read one tile ahead
+  // (gate_value), so that the wait for them falls where nothing else is in flight: a
+  // wait right behind the direct loads of a tile would wait for those too (the
+  // compiler does not count them and waits for every load).
+  const bool gate_lane = GATED && w == 0 && l < T::BN;
+  auto gate_value = [&](int t) {
+    const int key = t * T::BN + l;
+    return Gg[key < lastk ? key : lastk];
+  };
+  auto store_table = [&](int t, float g) {
+    if (gate_lane) {
       float* tab = reinterpret_cast<float*>(smem + (t % T::NSTAGE) * T::STAGE + 2 * T::TILE);
       const int key = t * T::BN + l;
-      const float g = Gg[key < lastk ? key : lastk];
       const bool keep = key < nk && !(key >= a.gate_sink && g < a.gate_tau);
       tab[l] = keep ? c2s - __builtin_amdgcn_logf(g + a.gate_eps) : __builtin_inff();
       tab[T::BN + l] = keep ? g : 0.0f;
     }
+  };
+  float gfirst = 0.0f, gnext = 0.0f;   // gate values for the tables of tiles 0 and t + 1
+  // first two tiles: gate values and direct loads; the table of tile 0 is written once
+  // the loads issued after them are awaited, before the barrier that publishes the tile
+  auto start_ring = [&]() {
+    if (gate_lane && ntiles > 0) gfirst = gate_value(0);
+    if (gate_lane && ntiles > 1) gnext = gate_value(1);
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
   };
   // F16: P V runs on f16 operands where V allows. P is kept as 2^14 sigma (in [0, 2^14],
   // normal in f16 down to sigma = 2^-28) and rounded once to f16, 2^-11 relative, 8x
@@ -164,11 +181,7 @@ void fwd_kernel(const KArgs a) {
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && l == 0) vflag[t % T::NSTAGE] = 1;
   };
   if (F16 && threadIdx.x < T::NSTAGE) vflag[threadIdx.x] = 0;
-  if (ntiles > 0) {
-    issue_tile(0);
-    fill_table(0);
-  }
-  if (ntiles > 1) issue_tile(1);
+  start_ring();
 
   // Q rows as B operands: lane holds query q0 + 32qb + l%32, d = 16ks + 8(l/32) + 0..7.
   bf16x8 qop[QB][T::KS];
@@ -194,6 +207,7 @@ void fwd_kernel(const KArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) mass[qb] = 0.0f;
 
+  if (ntiles > 0) store_table(0, gfirst);
   wait_vmem_and_barrier();
 
   // S of unit 0 (chunk 0, query block 0)
@@ -353,8 +367,12 @@ void fwd_kernel(const KArgs a) {
     const int st1 = SG >= 0 ? (SG + 1) % T::NSTAGE : (t + 1) % T::NSTAGE;
     // every thread reads the flag after the barrier that follows all its writers
     if constexpr (OPF16) vbad |= vflag[st];
-    if (t + 2 < ntiles) issue_tile(t + 2);
-    if (t + 1 < ntiles) fill_table(t + 1);
+    // gnext was read during the previous tile (or before the first) and has arrived
+    if (t + 1 < ntiles) store_table(t + 1, gnext);
+    if (t + 2 < ntiles) {
+      if (gate_lane) gnext = gate_value(t + 2);
+      issue_tile(t + 2);
+    }
     if constexpr (OPF16) {
       // tile t+2's slot was last read at the start of tile t-1
       if (threadIdx.x == 0) vflag[(st + 2) % T::NSTAGE] = 0;
@@ -403,9 +421,8 @@ void fwd_kernel(const KArgs a) {
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt) acc[qb][dt] = zero16();
       }
-      issue_tile(0);
-      fill_table(0);
-      if (ntiles > 1) issue_tile(1);
+      start_ring();
+      if (ntiles > 0) store_table(0, gfirst);
       wait_vmem_and_barrier();
       s_cur = zero16();
 #pragma unroll
