@@ -54,7 +54,6 @@ template <int D, int CPT, bool CAUSAL, bool GATED, bool SPLIT, bool DG, bool VL>
 __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* smem,
                                           void* out_k, void* out_v) {
   using T = DkvTraits<D, CPT>;
-  constexpr bool PIPE = D == 64;
 
   const int l = lane_id(), w = wave_id();
   const int lk = 4 * (l >> 5);
@@ -92,8 +91,9 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
   int c_lo = CAUSAL ? (k0 - diag > 0 ? k0 - diag : 0) / 32 : 0;
   if (k0 >= nk) c_lo = nch;                 // all keys of this wave are padding
   // S of the first unit is formed before the tile loop when its tile is one of the two
-  // loaded first, else at the start of that unit (a causal shift can put it later)
-  const bool s_late = VL && CAUSAL && PIPE && c_lo < nch && c_lo / CPT > t0 + 1;
+  // loaded first, else at the start of that unit (with 32-query tiles the first chunks
+  // of waves 2 and 3 lie past them; a causal shift can put them later still)
+  const bool s_late = CAUSAL && c_lo < nch && c_lo / CPT > t0 + 1;
 
   const DirectPair<T::BQ, D, T::kWaves> dma(sl);
   auto issue_tile = [&](int t) {
@@ -128,7 +128,7 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
 
   // S of this wave's first chunk (its tile is one of the two loaded above)
   f32x16 s_cur = zero16();
-  if (PIPE && c_lo < nch && !s_late) {
+  if (c_lo < nch && !s_late) {
     const char* st = smem + ((c_lo / CPT) % T::NSTAGE) * T::STAGE;
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks)
@@ -178,7 +178,7 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
   //   2: dS = dP P (1 - P), bf16 of h = 0     | -
   //   3: bf16 of h = 1                        | dV, dK for the first query half of c
   //   4: -                                    | dV, dK for the second query half
-  // (the MFMA-only step overlaps the VALU steps of the other wave on the SIMD)
+  // (at d = 64 the MFMA-only step overlaps the VALU steps of the other wave on the SIMD)
   const LdsLane<D> lane;
   auto unit = [&](auto mode_tag, const char* Qc, const char* dOc, int qrow, const char* Qn,
                   int qn_row, int qb0) {
@@ -236,33 +236,6 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
     s_cur = s_next;
   };
 
-  // d = 128: no cross-unit pipelining (four times the operand registers)
-  auto unit_flat = [&](auto mode_tag, const char* Qc, const char* dOc, int qrow, int qb0) {
-    f32x16 dp = zero16();
-    s_cur = zero16();
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) {
-      s_cur = mfma(lds_row_operand<D>(Qc, qrow, 16 * ks), kreg[ks], s_cur);
-      dp = mfma(lds_row_operand<D>(dOc, qrow, 16 * ks), vreg[ks], dp);
-    }
-    f32x16 p, ds;
-    sig16(mode_tag, qb0, p);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ds[r] = dp[r] * __builtin_fmaf(-p[r], p[r], p[r]);
-    if (DG) accumulate_ds(ds);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 ph, pl, dh, dl;
-      to_bf16(p, h, ph, pl);
-      to_bf16(ds, h, dh, dl);
-#pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) {
-        kv_mfma(dv[dt], lds_col_operand<D>(dOc, qrow + 16 * h, 32 * dt), ph, pl);
-        kv_mfma(dk[dt], lds_col_operand<D>(Qc, qrow + 16 * h, 32 * dt), dh, dl);
-      }
-    }
-  };
-
   // Tile loops: [t0, tm1) masked (the causal diagonal chunk), [tm1, tm2) interior,
   // [tm2, ntiles) masked (the tile holding the last valid query when nq % 32 != 0 or
   // when it holds fewer than CPT chunks).
@@ -293,18 +266,14 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
     for (int cc = 0; cc < CPT; ++cc) {
       const int c = t * CPT + cc;
       if (MODE == kKvInterior || (c >= c_lo && c < nch)) {
-        if (PIPE) {
-          if (MODE == kKvMasked && s_late && c == c_lo) {
-            s_cur = zero16();
+        if (MODE == kKvMasked && s_late && c == c_lo) {
+          s_cur = zero16();
 #pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks)
-              s_cur = mfma(lds_row_operand<D>(cur, cc * 32, 16 * ks), kreg[ks], s_cur);
-          }
-          const char* Qn = (cc + 1 < CPT) ? cur : nxt;
-          unit(mode_tag, cur, cur + T::TILE, cc * 32, Qn, ((cc + 1) % CPT) * 32, c * 32);
-        } else {
-          unit_flat(mode_tag, cur, cur + T::TILE, cc * 32, c * 32);
+          for (int ks = 0; ks < T::KS; ++ks)
+            s_cur = mfma(lds_row_operand<D>(cur, cc * 32, 16 * ks), kreg[ks], s_cur);
         }
+        const char* Qn = (cc + 1 < CPT) ? cur : nxt;
+        unit(mode_tag, cur, cur + T::TILE, cc * 32, Qn, ((cc + 1) % CPT) * 32, c * 32);
       }
     }
   };
@@ -317,12 +286,10 @@ __device__ __forceinline__ void dkdv_body(const KArgs& a, const Item& it, char* 
     // of the ring with compile-time slots
     int t = tm1;
     for (; t < tm2 && t % T::NSTAGE != 0; ++t) tile_body(Int{}, Dyn{}, t);
-    if (PIPE) {
-      for (; t + 3 <= tm2; t += 3) {
-        tile_body(Int{}, std::integral_constant<int, 0>{}, t);
-        tile_body(Int{}, std::integral_constant<int, 1>{}, t + 1);
-        tile_body(Int{}, std::integral_constant<int, 2>{}, t + 2);
-      }
+    for (; t + 3 <= tm2; t += 3) {
+      tile_body(Int{}, std::integral_constant<int, 0>{}, t);
+      tile_body(Int{}, std::integral_constant<int, 1>{}, t + 1);
+      tile_body(Int{}, std::integral_constant<int, 2>{}, t + 2);
     }
     for (; t < tm2; ++t) tile_body(Int{}, Dyn{}, t);
   }
