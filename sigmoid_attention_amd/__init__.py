@@ -12,6 +12,7 @@ raises, there is no fallback.
     dk, dv = bwd_dkdv(q, k, v, do, seqlens, ...)
     dq, dk, dv = bwd(q, k, v, do, seqlens, ...)            # both backward kernels, one call
     dk, dv, dg_head, dg = bwd_dkdv_dg(q, k, v, do, seqlens, gate=g, ...)
+    o = attention(q, k, v, seqlens, ...)                   # the same, under torch.autograd
     o = fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k)      # packed [rows, H, d] batches
     dq, dk, dv = bwd_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k)
     cache = KVCache(B, H, d, cap, gated=True, tau=0.05)   # KV cache with eviction
@@ -31,10 +32,10 @@ import os
 
 import numpy as np
 
-__all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd", "bwd_dkdv_dg", "fwd_varlen",
-           "bwd_dq_varlen", "bwd_dkdv_varlen", "bwd_varlen", "VarlenDesc", "KVCache",
-           "CacheDesc", "validate", "plan", "calibrate_mfma", "library_path", "load",
-           "Problem", "SigattnError", "STATUS", "VERSION", "NOALLOC_WORKSPACE_BYTES"]
+__all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd", "bwd_dkdv_dg", "attention",
+           "fwd_varlen", "bwd_dq_varlen", "bwd_dkdv_varlen", "bwd_varlen", "VarlenDesc",
+           "KVCache", "CacheDesc", "validate", "plan", "calibrate_mfma", "library_path",
+           "load", "Problem", "SigattnError", "STATUS", "VERSION", "NOALLOC_WORKSPACE_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsigattn.so")
@@ -457,6 +458,56 @@ def fwd_rowsum(q, k, v, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, ep
     del keep
     _check(code, "sigattn_fwd_rowsum")
     return out, row_mass
+
+
+_ATTENTION_FN = None
+
+
+def _attention_function():
+    """The torch.autograd.Function behind attention(), defined on first use (torch is
+    imported lazily by this module)."""
+    global _ATTENTION_FN
+    if _ATTENTION_FN is None:
+        torch = _torch()
+
+        class SigmoidAttention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, gate, seqlens, opts):
+                o = fwd(q, k, v, seqlens, gate=gate, **opts)
+                ctx.save_for_backward(q, k, v, gate)
+                ctx.seqlens = seqlens
+                ctx.opts = opts
+                return o
+
+            @staticmethod
+            def backward(ctx, grad_o):
+                q, k, v, gate = ctx.saved_tensors
+                # dO enters the kernels in q's dtype and layout
+                do = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+                do.copy_(grad_o)
+                opts = dict(ctx.opts, out_dtype=None)   # gradients in the inputs' dtype
+                if gate is not None and ctx.needs_input_grad[3]:
+                    dq = bwd_dq(q, k, v, do, ctx.seqlens, gate=gate, **opts)
+                    dk, dv, _, dg = bwd_dkdv_dg(q, k, v, do, ctx.seqlens, gate=gate, **opts)
+                else:
+                    dq, dk, dv = bwd(q, k, v, do, ctx.seqlens, gate=gate, **opts)
+                    dg = None
+                return dq, dk, dv, dg, None, None
+
+        _ATTENTION_FN = SigmoidAttention
+    return _ATTENTION_FN
+
+
+def attention(q, k, v, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, eps=1e-8,
+              scale=0.0, bias=None, out_dtype=None, fast_math=False):
+    """O as fwd, differentiable with torch.autograd: the backward calls bwd (one call for
+    dQ, dK, dV), or bwd_dq and bwd_dkdv_dg when the gate also needs its gradient (the
+    gate's gradient is the head sum of the per-head one; dropped and padded keys get 0).
+    The incoming gradient is copied into q's dtype and layout, and the gradients come out
+    in q's dtype. seqlens, tau, sink, eps, scale and bias are constants."""
+    opts = dict(causal=causal, tau=tau, sink=sink, eps=eps, scale=scale, bias=bias,
+                out_dtype=out_dtype, fast_math=fast_math)
+    return _attention_function().apply(q, k, v, gate, seqlens, opts)
 
 
 class KVCache:

@@ -1,0 +1,82 @@
+"""The autograd entry point (sigmoid_attention_amd.attention) on the GPU: its output and
+the gradients torch.autograd returns are bitwise those of the direct calls with the same
+rounded dO (fwd; bwd, or bwd_dq and bwd_dkdv_dg when the gate needs a gradient), and
+they match the fp64 oracle at the stated bar."""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import (BF16_TOL, check_all, check_bounds, need_gpu, note, oracle_full,
+                      oracle_magnitudes)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "bidir": dict(),
+    "causal_gated": dict(causal=True, gate=("logistic_normal", 2.0, 2.0, 0.3, 0.01), tau=0.05,
+                         sink=4),
+}
+
+
+def _inputs(torch, case, d):
+    w = W.Workload(f"autograd_{case}_{d}", "bf16", 3, 2, d, 200, ("fixed", [200, 77, 1]),
+                   seed=700 + d, **CASES[case])
+    data = W.generate(w)
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(data[k]).to(torch.bfloat16).to(dev) for k in ("q", "k", "v", "do")}
+    gate = None if data["gate"] is None else torch.from_numpy(data["gate"]).to(dev)
+    return w, data, t, gate
+
+
+@pytest.mark.parametrize("case,gate_grad", [("bidir", False), ("causal_gated", False),
+                                             ("causal_gated", True)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_autograd_matches_direct_calls(d, case, gate_grad):
+    torch = need_gpu()
+    import sigmoid_attention_amd as S
+    w, data, t, gate = _inputs(torch, case, d)
+    note(f"autograd d={d} {case} gate_grad={gate_grad}")
+    kw = dict(causal=w.causal, tau=w.tau, sink=w.sink, out_dtype=torch.float32)
+    q, k, v = (t[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    g = None if gate is None else gate.clone().requires_grad_(gate_grad)
+    o = S.attention(q, k, v, data["seqlens"], gate=g, **kw)
+    o.backward(t["do"].float())          # dO as float; the entry point rounds it to bf16
+    torch.cuda.synchronize()
+
+    o_ref = S.fwd(t["q"], t["k"], t["v"], data["seqlens"], gate=gate, **kw)
+    dkw = dict(causal=w.causal, tau=w.tau, sink=w.sink, gate=gate)
+    dq, dk, dv = S.bwd(t["q"], t["k"], t["v"], t["do"], data["seqlens"], **dkw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for name, got, ref in (("dQ", q.grad, dq), ("dK", k.grad, dk), ("dV", v.grad, dv)):
+        assert got.dtype == torch.bfloat16
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), name
+    if gate_grad:
+        _, _, _, dg = S.bwd_dkdv_dg(t["q"], t["k"], t["v"], t["do"], data["seqlens"], **dkw)
+        torch.cuda.synchronize()
+        assert torch.equal(g.grad, dg)
+    elif g is not None:
+        assert g.grad is None
+
+
+def test_autograd_against_oracle():
+    """Float output of the forward at the bar; the bf16 gradients within the element-wise
+    bounds that add their own bf16 rounding (the bounds the parity tests use for bf16
+    outputs)."""
+    torch = need_gpu()
+    import sigmoid_attention_amd as S
+    w, data, t, gate = _inputs(torch, "causal_gated", 64)
+    note("autograd against the oracle")
+    q, k, v = (t[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    o = S.attention(q, k, v, data["seqlens"], gate=gate, causal=True, tau=w.tau, sink=w.sink,
+                    out_dtype=torch.float32)
+    o.backward(t["do"].float())
+    torch.cuda.synchronize()
+    ref = oracle_full(data)
+    print(check_all({"O": o.detach().cpu().numpy()}, ref, data["seqlens"], BF16_TOL,
+                    "autograd O"))
+    grads = {"dQ": q.grad.float().cpu().numpy(), "dK": k.grad.float().cpu().numpy(),
+             "dV": v.grad.float().cpu().numpy()}
+    print(check_bounds(grads, ref, oracle_magnitudes(data), data["seqlens"], True, False,
+                       "autograd gradients"))

@@ -121,3 +121,14 @@ def test_problem_rejects_overlapping_rows(strides, ok):
     overlap (checked by sigattn_validate on the host)."""
     p, keep = S.make_problem(2, 2, 64, 64, [64, 30], strides=strides)
     assert S.validate(p) == (0 if ok else 1)
+
+
+def test_attention_is_checked_like_fwd():
+    """The autograd entry point goes through the same checks before any launch."""
+    q, k, v = _qkv()
+    for t in (q, k, v):
+        t.requires_grad_(True)
+    with pytest.raises(ValueError, match="same GPU"):
+        S.attention(q, k, v, [64, 10])
+    with pytest.raises(ValueError, match="gate must be a float32"):
+        S.attention(q, k, v, [64, 10], gate=torch.ones((1, 64), dtype=torch.float32))
