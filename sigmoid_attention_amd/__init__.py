@@ -15,6 +15,7 @@ raises, there is no fallback.
     o = attention(q, k, v, seqlens, ...)                   # the same, under torch.autograd
     o = fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k)      # packed [rows, H, d] batches
     dq, dk, dv = bwd_varlen(q, k, v, do, cu_q, cu_k, max_q, max_k)
+    o = attention_varlen(q, k, v, cu_q, cu_k, max_q, max_k)  # the same under torch.autograd
     cache = KVCache(B, H, d, cap, gated=True, tau=0.05)   # KV cache with eviction
     cache.build(k, v, seqlens, gate=g); cache.append(k1, v1, g1); o1 = cache.decode(q1, bias)
     o1 = cache.decode_noalloc(q1, bias, out=o1)              # no workspace, no allocation
@@ -33,9 +34,10 @@ import os
 import numpy as np
 
 __all__ = ["fwd", "fwd_rowsum", "bwd_dq", "bwd_dkdv", "bwd", "bwd_dkdv_dg", "attention",
-           "fwd_varlen", "bwd_dq_varlen", "bwd_dkdv_varlen", "bwd_varlen", "VarlenDesc",
-           "KVCache", "CacheDesc", "validate", "plan", "calibrate_mfma", "library_path",
-           "load", "Problem", "SigattnError", "STATUS", "VERSION", "NOALLOC_WORKSPACE_BYTES"]
+           "attention_varlen", "fwd_varlen", "bwd_dq_varlen", "bwd_dkdv_varlen", "bwd_varlen",
+           "VarlenDesc", "KVCache", "CacheDesc", "validate", "plan", "calibrate_mfma",
+           "library_path", "load", "Problem", "SigattnError", "STATUS", "VERSION",
+           "NOALLOC_WORKSPACE_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsigattn.so")
@@ -496,6 +498,65 @@ def _attention_function():
 
         _ATTENTION_FN = SigmoidAttention
     return _ATTENTION_FN
+
+
+def _zeros_like_layout(x, dtype):
+    """Zeros with x's shape and strides (dtype None: x's dtype)."""
+    torch = _torch()
+    return torch.empty_strided(x.shape, x.stride(), dtype=x.dtype if dtype is None else dtype,
+                               device=x.device).zero_()
+
+
+_ATTENTION_VARLEN_FN = None
+
+
+def _attention_varlen_function():
+    global _ATTENTION_VARLEN_FN
+    if _ATTENTION_VARLEN_FN is None:
+        torch = _torch()
+
+        class SigmoidAttentionVarlen(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, gate, bias, opts):
+                # rows outside every sequence are not written by the kernels: start from 0
+                o = _zeros_like_layout(q, opts["out_dtype"])
+                fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, gate=gate, bias=bias, out=o,
+                           **opts)
+                ctx.save_for_backward(q, k, v, cu_q, cu_k, gate, bias)
+                ctx.bounds = (max_q, max_k)
+                ctx.opts = opts
+                return o
+
+            @staticmethod
+            def backward(ctx, grad_o):
+                q, k, v, cu_q, cu_k, gate, bias = ctx.saved_tensors
+                do = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+                do.copy_(grad_o)
+                opts = dict(ctx.opts, out_dtype=None)
+                out = (_zeros_like_layout(q, None), _zeros_like_layout(k, None),
+                       _zeros_like_layout(k, None))
+                dq, dk, dv = bwd_varlen(q, k, v, do, cu_q, cu_k, *ctx.bounds, gate=gate,
+                                        bias=bias, out=out, **opts)
+                return dq, dk, dv, None, None, None, None, None, None, None
+
+        _ATTENTION_VARLEN_FN = SigmoidAttentionVarlen
+    return _ATTENTION_VARLEN_FN
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, max_q, max_k, *, causal=False, gate=None, tau=0.0,
+                     sink=4, eps=1e-8, scale=0.0, bias=None, out_dtype=None, fast_math=False):
+    """O as fwd_varlen, differentiable with torch.autograd (the backward calls bwd_varlen).
+    Rows outside every sequence are 0 in O and in the gradients (the outputs start from
+    zeros, which the kernels leave there). The packed entry points have no gate gradient,
+    so a gate that requires one is refused; cu_q, cu_k, the bounds, the gate and the bias
+    are constants."""
+    if gate is not None and getattr(gate, "requires_grad", False):
+        raise ValueError("the packed entry points have no gate gradient: use attention() on "
+                         "padded tensors, or pass a gate that does not require grad")
+    opts = dict(causal=causal, tau=tau, sink=sink, eps=eps, scale=scale, out_dtype=out_dtype,
+                fast_math=fast_math)
+    return _attention_varlen_function().apply(q, k, v, cu_q, cu_k, max_q, max_k, gate, bias,
+                                              opts)
 
 
 def attention(q, k, v, seqlens, *, causal=False, gate=None, tau=0.0, sink=4, eps=1e-8,

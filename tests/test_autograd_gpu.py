@@ -1,7 +1,10 @@
-"""The autograd entry point (sigmoid_attention_amd.attention) on the GPU: its output and
-the gradients torch.autograd returns are bitwise those of the direct calls with the same
-rounded dO (fwd; bwd, or bwd_dq and bwd_dkdv_dg when the gate needs a gradient), and
-they match the fp64 oracle at the stated bar."""
+"""The autograd entry points (sigmoid_attention_amd.attention and attention_varlen) on
+the GPU: the output and the gradients torch.autograd returns are bitwise those of the
+direct calls with the same rounded dO (fwd; bwd, or bwd_dq and bwd_dkdv_dg when the gate
+needs a gradient; fwd_varlen and bwd_varlen for packed batches), and they match the fp64
+oracle at the stated bar."""
+
+import math
 
 import numpy as np
 import pytest
@@ -80,3 +83,53 @@ def test_autograd_against_oracle():
              "dV": v.grad.float().cpu().numpy()}
     print(check_bounds(grads, ref, oracle_magnitudes(data), data["seqlens"], True, False,
                        "autograd gradients"))
+
+
+def _packed(torch, seed, lens_q, lens_k, H, d, gated, extra_rows=5):
+    """Packed bf16 q, k, v, dO with rows past the last sequence, cu arrays on the device."""
+    rng = np.random.default_rng(seed)
+    tq, tk = int(np.sum(lens_q)) + extra_rows, int(np.sum(lens_k)) + extra_rows
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(rng.standard_normal((tq if n in ("q", "do") else tk, H, d),
+                                                 dtype=np.float32)).to(torch.bfloat16).to(dev)
+         for n in ("q", "k", "v", "do")}
+    gate = None
+    if gated:
+        g = 1.0 / (1.0 + np.exp(-(rng.standard_normal(tk) * math.sqrt(2.0) + 1.0)))
+        g[rng.random(tk) < 0.2] = 0.01
+        gate = torch.from_numpy(g.astype(np.float32)).to(dev)
+    cu = [torch.from_numpy(np.concatenate([[0], np.cumsum(x)]).astype(np.int32)).to(dev)
+          for x in (lens_q, lens_k)]
+    return t, gate, cu[0], cu[1], int(max(lens_q)), int(max(lens_k))
+
+
+@pytest.mark.parametrize("causal,gated", [(False, False), (True, True)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_varlen_matches_direct_calls(d, causal, gated):
+    """Unequal query and key lengths (one empty key set, one 1-row query) and five rows
+    past the last sequence, which come out 0 in O and in every gradient."""
+    torch = need_gpu()
+    import sigmoid_attention_amd as S
+    lens_q, lens_k = [128, 300, 40, 1, 200], [700, 300, 9, 33, 0]
+    t, gate, cu_q, cu_k, mq, mk = _packed(torch, 900 + d, lens_q, lens_k, 2, d, gated)
+    note(f"attention_varlen d={d} causal={causal} gated={gated}")
+    kw = dict(causal=causal, gate=gate, tau=0.05 if gated else 0.0, sink=4)
+    q, k, v = (t[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    o = S.attention_varlen(q, k, v, cu_q, cu_k, mq, mk, out_dtype=torch.float32, **kw)
+    o.backward(t["do"].float())
+    torch.cuda.synchronize()
+
+    o_ref = torch.zeros(t["q"].shape, dtype=torch.float32, device=o.device)
+    S.fwd_varlen(t["q"], t["k"], t["v"], cu_q, cu_k, mq, mk, out=o_ref, out_dtype=torch.float32,
+                 **kw)
+    refs = (torch.zeros_like(t["q"]), torch.zeros_like(t["k"]), torch.zeros_like(t["k"]))
+    S.bwd_varlen(t["q"], t["k"], t["v"], t["do"], cu_q, cu_k, mq, mk, out=refs, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    nq, nk = sum(lens_q), sum(lens_k)
+    assert torch.count_nonzero(o[nq:]) == 0
+    for name, got, ref, n in (("dQ", q.grad, refs[0], nq), ("dK", k.grad, refs[1], nk),
+                              ("dV", v.grad, refs[2], nk)):
+        assert got.dtype == torch.bfloat16
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), name
+        assert torch.count_nonzero(got[n:]) == 0, name

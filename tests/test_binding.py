@@ -132,3 +132,16 @@ def test_attention_is_checked_like_fwd():
         S.attention(q, k, v, [64, 10])
     with pytest.raises(ValueError, match="gate must be a float32"):
         S.attention(q, k, v, [64, 10], gate=torch.ones((1, 64), dtype=torch.float32))
+
+
+def test_attention_varlen_refuses_a_gate_gradient():
+    """The packed entry points have no gate gradient, so a gate that asks for one is
+    refused before anything is allocated; otherwise the same checks as fwd_varlen."""
+    q, k, v, do, cu_q, cu_k = _packed()
+    for t in (q, k, v):
+        t.requires_grad_(True)
+    gate = torch.ones(12, dtype=torch.float32, requires_grad=True)
+    with pytest.raises(ValueError, match="no gate gradient"):
+        S.attention_varlen(q, k, v, cu_q, cu_k, 10, 12, gate=gate)
+    with pytest.raises(ValueError, match="same shape"):
+        S.attention_varlen(q, k, v[:3], cu_q, cu_k, 10, 12)
