@@ -312,10 +312,14 @@ sigattn_status sigattn_decode_noalloc(const sigattn_cache* c, const void* q, int
                                       int32_t out_dtype, void* stream);
 
 /* Host-side view of the work list a pass launches, for inspection and tests.
- * pass: 0 forward, 1 dq, 2 dk/dv. Writes up to `cap` items as (b, h, tile) int32
- * triples into `items` (may be NULL when cap is 0) in launch order, and the tile
- * height in rows into *tile_rows (may be NULL). Returns the number of compute items,
- * or -1 if the problem is invalid. Fully padded tiles never appear. */
+ * pass: 0 forward, 1 dq, 2 dk/dv, 3 the one-call backward of sigattn_bwd (d = 64 only),
+ * whose dQ items are written as (b, h, -1 - tile). Writes up to `cap` items as
+ * (b, h, tile) int32 triples into `items` (may be NULL when cap is 0) in launch order,
+ * and the tile height in rows into *tile_rows (may be NULL). Returns the number of
+ * compute items, or -1 if the problem is invalid. Fully padded tiles never appear.
+ * Causal batches whose sequences all have one length are listed tile by tile (every
+ * (sequence, head) of one tile together), costliest tiles first; in the one-call list
+ * the dK/dV and dQ tiles are interleaved by cost. */
 int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int64_t cap,
                      int32_t* tile_rows);
 

@@ -245,7 +245,9 @@ def validate(problem: Problem) -> int:
 
 
 def plan(problem: Problem, pass_: int):
-    """Work list of a pass as an int32 array [n, 3] of (b, h, tile), and the tile height."""
+    """Work list of a pass (0 forward, 1 dQ, 2 dK/dV, 3 the one-call backward at d = 64,
+    whose dQ items carry tile -1 - t) as an int32 array [n, 3] of (b, h, tile) in launch
+    order, and the tile height."""
     lib = load()
     tile = ctypes.c_int32(0)
     n = lib.sigattn_plan(ctypes.byref(problem), pass_, None, 0, ctypes.byref(tile))

@@ -1,6 +1,7 @@
 // Both backward kernels in one launch (d = 64, padded or packed batches): the work list
-// is the dK/dV pass's items followed by the dQ pass's items, each workgroup running the
-// body of the pass its item belongs to. The bodies, their arithmetic and their outputs are those of the separate
+// is the dK/dV pass's items followed by the dQ pass's items (for causal batches of one
+// length, both passes' tile blocks merged by cost), each workgroup running the body of
+// the pass its item belongs to. The bodies, their arithmetic and their outputs are those of the separate
 // dQ and dK/dV kernels ("Better Models, Faster Training: Sigmoid Attention for
 // single-cell Foundation Models", section 4: one kernel for dQ, one for dK/dV, no
 // atomics); only the dispatch is shared, so the workgroups of one pass fill the slots
@@ -20,17 +21,23 @@ void bwd_kernel(const KArgs a, void* dq, int nq_items, int tiles_q) {
   constexpr int kBytesQ = TQ::NSTAGE * TQ::STAGE, kBytesK = TK::NSTAGE * TK::STAGE;
   __shared__ __attribute__((aligned(1024))) char smem[kBytesQ > kBytesK ? kBytesQ : kBytesK];
   const int g = remap_block(blockIdx.x, a.nitems + nq_items, a.xcd_chunk);
-  if (g < a.nitems) {
-    const Item it = uniform_item(VL ? varlen_item(a, g, a.tiles_per_seq, 1) : decode_item(a, g, 0));
-    if (VL && !it.valid) return;
-    dkdv_body<64, 2, CAUSAL, GATED, SPLIT, false, VL>(a, it, smem, a.out0, a.out1);
+  bool dq_item = g >= a.nitems;
+  Item it;
+  if (!VL && CAUSAL && a.nblocks > 0) {
+    it = decode_block_item(a, g, &dq_item);          // both passes' blocks, merged by cost
+  } else if (!dq_item) {
+    it = VL ? varlen_item(a, g, a.tiles_per_seq, 1) : decode_item(a, g, 0);
   } else {
     const int gq = g - a.nitems;
-    const Item it = uniform_item(VL ? varlen_item(a, gq, tiles_q, 0)
-                                    : decode_item(a, gq, CAUSAL ? 1 : 0));
-    if (VL && !it.valid) return;
-    dq_body<64, 2, CAUSAL, GATED, SPLIT, VL>(a, it, smem, dq);
+    it = VL ? varlen_item(a, gq, tiles_q, 0) : decode_item(a, gq, CAUSAL ? 1 : 0);
   }
+  it = uniform_item(it);
+  dq_item = __builtin_amdgcn_readfirstlane(dq_item ? 1 : 0) != 0;
+  if (VL && !it.valid) return;
+  if (!dq_item)
+    dkdv_body<64, 2, CAUSAL, GATED, SPLIT, false, VL>(a, it, smem, a.out0, a.out1);
+  else
+    dq_body<64, 2, CAUSAL, GATED, SPLIT, VL>(a, it, smem, dq);
 }
 
 template <bool C, bool G, bool SP>

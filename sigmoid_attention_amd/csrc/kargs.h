@@ -10,7 +10,15 @@
 // contiguous chunk of items per round, so that the tiles sharing one head's K/V run on
 // the same XCD and its L2.
 //
-// Packed variable-length batches (device-side cu_seqlens) use a second mode: the grid is
+// Causal batches whose sequences all have one length (fixed-length training batches) are
+// listed block-major instead: one block per tile index, holding that tile of every
+// (sequence, head), the blocks in decreasing cost, so that list scheduling starts the
+// longest items first across the whole batch and not only within each sequence. In the
+// one-call backward the blocks of both passes are merged by cost. The remap is off in
+// this mode (blockIdx = item): with a multiple of 8 (sequence, head) pairs per block,
+// every tile of one head then lands on the same XCD.
+//
+// Packed variable-length batches (device-side cu_seqlens) use a third mode: the grid is
 // B x H x ceil(max_rows / tile) items in (b, h, tile) order with the tile fastest, each
 // workgroup reads its sequence's bounds from device memory and exits at once when its
 // tile starts past the sequence's rows. Query and key lengths may differ; the causal
@@ -29,6 +37,8 @@ namespace sa {
 
 constexpr int kMaxBatch = 256;
 constexpr int kNumXcd = 8;
+constexpr int kMaxBlocks = 128;       // block-major lists: at most this many tile blocks
+constexpr unsigned kDqBlock = 0x8000u;  // block code bit: a dQ block of the one-call list
 
 struct KArgs {
   const void* q;
@@ -64,6 +74,11 @@ struct KArgs {
   const int32_t* cu_q;         // device [B + 1] query row bounds
   const int32_t* cu_k;         // device [B + 1] key row bounds
   const float* bias;           // device [B] or null (then beta_b = -ln(nk_b))
+  // block-major mode (nblocks > 0; padded causal batches of one length): item g is
+  // (sorted position, head) (g % (nsorted * H)) / H, g % H of block g / (nsorted * H),
+  // whose code holds the tile index (low 15 bits) and kDqBlock
+  int32_t nblocks;
+  uint16_t blocks[kMaxBlocks];
   int32_t off[kMaxBatch + 1];  // prefix item counts by sorted position
   float c2[kMaxBatch];         // -beta * log2(e) by sorted position
   uint16_t len[kMaxBatch];     // valid length by sorted position
@@ -97,35 +112,58 @@ SA_HD inline int remap_block(int w, int nitems, int chunk) {
   return (s / chunk) * round + x * chunk + (s % chunk);
 }
 
-// `reverse` lists a sequence's tiles last-first (the causal query-side passes).
+// Item (head h, tile t) of the sequence at sorted position p.
+SA_HD inline Item item_at(const KArgs& a, int p, int h, int t) {
+  Item it;
+  it.b = a.bidx[p];
+  it.nq = it.nk = a.len[p];
+  it.diag = 0;
+  it.valid = 1;
+  it.c2 = a.c2[p];
+  it.h = h;
+  it.t = t;
+  it.qoff = it.koff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
+  it.goff = (int64_t)it.b * a.gsb;
+  return it;
+}
+
+// Item g of a block-major list; *dq_block is set for a dQ block of the one-call list.
+SA_HD inline Item decode_block_item(const KArgs& a, int g, bool* dq_block) {
+  const int m = a.nsorted * a.H;
+  const int blk = g / m;
+  const int r = g - blk * m;
+  const int p = r / a.H;
+  const unsigned code = a.blocks[blk];
+  *dq_block = (code & kDqBlock) != 0u;
+  return item_at(a, p, r - p * a.H, (int)(code & (kDqBlock - 1u)));
+}
+
+// `reverse` lists a sequence's tiles last-first (the causal query-side passes); a
+// block-major list carries its tile order in the block codes instead.
 SA_HD inline Item decode_item(const KArgs& a, int g, int reverse) {
+  if (a.nblocks > 0) {
+    bool dq_block;
+    return decode_block_item(a, g, &dq_block);
+  }
   // largest p with off[p] <= g (off is non-decreasing, off[0] = 0)
   int lo = 0, hi = a.nsorted - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (a.off[mid] <= g) lo = mid; else hi = mid - 1;
   }
-  Item it;
   const int p = lo;
-  it.b = a.bidx[p];
-  const int n = a.len[p];
-  it.nq = it.nk = n;
-  it.diag = 0;
-  it.valid = 1;
-  it.c2 = a.c2[p];
-  const int T = (n + a.tile - 1) / a.tile;
+  const int T = (a.len[p] + a.tile - 1) / a.tile;
   const int local = g - a.off[p];
+  int h, t;
   if (a.causal) {
-    it.h = local % a.H;
-    it.t = local / a.H;
+    h = local % a.H;
+    t = local / a.H;
   } else {
-    it.h = local / T;
-    it.t = local % T;
+    h = local / T;
+    t = local % T;
   }
-  if (reverse) it.t = T - 1 - it.t;
-  it.qoff = it.koff = (int64_t)it.b * a.sb + (int64_t)it.h * a.sh;
-  it.goff = (int64_t)it.b * a.gsb;
-  return it;
+  if (reverse) t = T - 1 - t;
+  return item_at(a, p, h, t);
 }
 
 SA_HD inline Item decode_item(const KArgs& a, int g) { return decode_item(a, g, a.reverse); }

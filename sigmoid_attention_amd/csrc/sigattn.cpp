@@ -167,6 +167,50 @@ int xcd_chunk_default() {
   return v;
 }
 
+// 32 x 32 units of work in tile t of a causal sequence of n rows (tiles of `tile` rows,
+// one 32-row slice per wave): a query slice sees the keys up to its last row, a key
+// slice the queries from its first row on.
+double causal_tile_units(int n, int tile, int t, bool key_side) {
+  const int slices = (n + 31) / 32;
+  double u = 0.0;
+  for (int w = 0; w < tile / 32; ++w) {
+    const int r = t * (tile / 32) + w;
+    if (r >= slices) break;
+    u += key_side ? slices - r : r + 1;
+  }
+  return u;
+}
+
+// Measured cost of a dK/dV unit relative to a dQ unit (1.46 and 1.03 us per wave at two
+// waves per SIMD), which orders the merged blocks of the one-call backward.
+constexpr double kDkdvUnitCost = 1.42;
+
+// Block-major list for a causal batch whose sequences all have one length: one block per
+// tile, costliest first. `which` is the pass (0 forward, 1 dQ, 2 dK/dV) or 3 for the
+// one-call backward, whose dK/dV and dQ blocks are merged by cost (dQ blocks flagged).
+// Other batches, and lists of more than kMaxBlocks blocks, keep the per-sequence order.
+void order_blocks(KArgs* a, int which) {
+  a->nblocks = 0;
+  if (!a->causal || a->nsorted == 0 || a->len[0] != a->len[a->nsorted - 1]) return;
+  const int n = a->len[0];
+  const int T = (n + a->tile - 1) / a->tile;
+  struct Block { double cost; uint16_t code; };
+  std::vector<Block> blocks;
+  if (which == 2 || which == 3)
+    for (int t = 0; t < T; ++t)
+      blocks.push_back({kDkdvUnitCost * causal_tile_units(n, a->tile, t, true), (uint16_t)t});
+  if (which != 2)
+    for (int t = T - 1; t >= 0; --t)
+      blocks.push_back({causal_tile_units(n, a->tile, t, false),
+                        (uint16_t)(t | (which == 3 ? sa::kDqBlock : 0u))});
+  if ((int)blocks.size() > sa::kMaxBlocks) return;
+  std::stable_sort(blocks.begin(), blocks.end(),
+                   [](const Block& x, const Block& y) { return x.cost > y.cost; });
+  a->nblocks = (int)blocks.size();
+  for (int i = 0; i < a->nblocks; ++i) a->blocks[i] = blocks[i].code;
+  a->xcd_chunk = 0;
+}
+
 // Fill the kernel-argument block of one pass: the sorted, padded-tile-free work list.
 void plan_pass(const sigattn_problem* p, int pass, KArgs* a) {
   std::memset(a, 0, sizeof(*a));
@@ -207,6 +251,7 @@ void plan_pass(const sigattn_problem* p, int pass, KArgs* a) {
   a->gate_sink = p->gate_sink;
   a->out_f32 = p->out_dtype == SIGATTN_F32 ? 1 : 0;
   a->f16_pv = (pass == 0 && p->fast_math == 2) ? 1 : 0;
+  order_blocks(a, pass);
 }
 
 bool needs_zero_fill(const sigattn_problem* p) {
@@ -574,6 +619,7 @@ sigattn_status sigattn_bwd(const sigattn_problem* p, const void* q, const void* 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   KArgs a;
   plan_pass(p, 2, &a);
+  order_blocks(&a, 3);
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = dk; a.out1 = dv;
   if (a.nitems > 0 && sa::launch_bwd_bf16(a, dq, a.nitems, 0, p->causal != 0, p->gate != nullptr,
                                           p->fast_math != 1, st) != hipSuccess)
@@ -739,19 +785,38 @@ sigattn_status sigattn_decode_noalloc(const sigattn_cache* c, const void* q, int
 
 int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int64_t cap,
                      int32_t* tile_rows_out) {
-  if (validate_problem(p) != SIGATTN_OK || pass < 0 || pass > 2) return -1;
+  if (validate_problem(p) != SIGATTN_OK || pass < 0 || pass > 3) return -1;
+  if (pass == 3 && p->d != 64) return -1;
   if (cap > 0 && !items) return -1;
   if (p->B == 0) return 0;
   KArgs a;
-  plan_pass(p, pass, &a);
+  plan_pass(p, pass == 3 ? 2 : pass, &a);
   if (tile_rows_out) *tile_rows_out = a.tile;
-  for (int w = 0; w < a.nitems && w < cap; ++w) {
-    const sa::Item it = sa::decode_item(a, sa::remap_block(w, a.nitems, a.xcd_chunk));
+  if (pass < 3) {
+    for (int w = 0; w < a.nitems && w < cap; ++w) {
+      const sa::Item it = sa::decode_item(a, sa::remap_block(w, a.nitems, a.xcd_chunk));
+      items[3 * w + 0] = it.b;
+      items[3 * w + 1] = it.h;
+      items[3 * w + 2] = it.t;
+    }
+    return a.nitems;
+  }
+  // the one-call backward: the dK/dV list, then the dQ list (the dQ pass's order with
+  // the dK/dV pass's tiles), or both merged block-major; dQ items as (b, h, -1 - tile)
+  order_blocks(&a, 3);
+  const int total = 2 * a.nitems;
+  for (int w = 0; w < total && w < cap; ++w) {
+    const int g = sa::remap_block(w, total, a.xcd_chunk);
+    bool dq_item = g >= a.nitems;
+    sa::Item it;
+    if (p->causal && a.nblocks > 0) it = sa::decode_block_item(a, g, &dq_item);
+    else if (!dq_item) it = sa::decode_item(a, g, 0);
+    else it = sa::decode_item(a, g - a.nitems, p->causal ? 1 : 0);
     items[3 * w + 0] = it.b;
     items[3 * w + 1] = it.h;
-    items[3 * w + 2] = it.t;
+    items[3 * w + 2] = dq_item ? -1 - it.t : it.t;
   }
-  return a.nitems;
+  return total;
 }
 
 sigattn_status sigattn_calibrate_mfma(int32_t nblocks, int32_t iters, float* sink,

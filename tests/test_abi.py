@@ -160,13 +160,17 @@ def test_empty_batch_is_a_noop(lib):
     assert S.plan(p, 0)[0].shape == (0, 3)
 
 
+MIXED = [1000, 0, 1, 4096, 257, 4096, 3000]
+ONE_LENGTH = [0, 1000, 1000, 1000, 0, 1000]     # one length (empty entries aside)
+
+
 @pytest.mark.parametrize("pass_", [0, 1, 2])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-def test_plan_covers_exactly_the_valid_tiles(lib, pass_, causal, d):
+@pytest.mark.parametrize("seqlens", [MIXED, ONE_LENGTH], ids=["mixed", "one_length"])
+def test_plan_covers_exactly_the_valid_tiles(lib, pass_, causal, d, seqlens):
     """Every tile holding a valid row is listed exactly once; fully padded tiles never
     appear (block-sparse padding, section 4 of the sigmoid-attention paper)."""
-    seqlens = [1000, 0, 1, 4096, 257, 4096, 3000]
     B, H, L = len(seqlens), 5, 4096
     p, keep = S.make_problem(B, H, L, d, seqlens, causal=causal)
     items, tile = S.plan(p, pass_)
@@ -175,6 +179,63 @@ def test_plan_covers_exactly_the_valid_tiles(lib, pass_, causal, d):
                   for t in range((n + tile - 1) // tile))
     assert got == want
     assert len(set(got)) == len(got)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("seqlens", [MIXED, ONE_LENGTH], ids=["mixed", "one_length"])
+def test_one_call_backward_list_covers_both_passes(lib, causal, seqlens):
+    """The one-call backward's list (d = 64) holds every dK/dV tile and every dQ tile
+    exactly once (dQ items reported with tile -1 - t); d = 128 has no such list."""
+    B, H, L = len(seqlens), 3, 4096
+    p, keep = S.make_problem(B, H, L, 64, seqlens, causal=causal)
+    items, tile = S.plan(p, 3)
+    want = sorted((b, h, t) for b, n in enumerate(seqlens) for h in range(H)
+                  for t in range((n + tile - 1) // tile))
+    got = items.tolist()
+    assert sorted(tuple(x) for x in got if x[2] >= 0) == want
+    assert sorted((b, h, -1 - t) for b, h, t in got if t < 0) == want
+    p128, keep128 = S.make_problem(B, H, L, 128, seqlens, causal=causal)
+    with pytest.raises(ValueError):
+        S.plan(p128, 3)
+
+
+def _causal_units(n, tile, t, key_side):
+    """32 x 32 units of a causal tile, counted directly over its 32-row slices."""
+    u = 0
+    for r in range(t * tile // 32, min((t + 1) * tile // 32, -(-n // 32))):
+        u += -(-n // 32) - r if key_side else r + 1
+    return u
+
+
+@pytest.mark.parametrize("pass_", [0, 1, 2, 3])
+def test_one_length_causal_batches_are_listed_tile_by_tile(lib, pass_):
+    """Causal batches of one length: each run of B * H consecutive items holds one tile
+    of every (sequence, head), the runs in non-increasing work (the one-call list weighs
+    a dK/dV unit 1.42 times a dQ unit), and item g runs on XCD g % 8, so that all tiles
+    of one head share an XCD when B * H is a multiple of 8."""
+    B, H, n = 4, 6, 1000
+    p, keep = S.make_problem(B, H, 1024, 64, [n] * B, causal=True)
+    items, tile = S.plan(p, pass_)
+    m = B * H
+    T = -(-n // tile)
+    assert len(items) == m * T * (2 if pass_ == 3 else 1)
+    costs = []
+    for blk in range(len(items) // m):
+        run = items[blk * m:(blk + 1) * m]
+        assert sorted((b, h) for b, h, _ in run.tolist()) == [(b, h) for b in range(B) for h in range(H)]
+        assert len(set(run[:, 2].tolist())) == 1
+        t = int(run[0, 2])
+        if pass_ == 3:
+            key_side = t >= 0
+            t = t if key_side else -1 - t
+            costs.append(_causal_units(n, tile, t, key_side) * (1.42 if key_side else 1.0))
+        else:
+            costs.append(_causal_units(n, tile, t, pass_ == 2))
+    assert costs == sorted(costs, reverse=True)
+    xcd = {}
+    for g, (b, h, _) in enumerate(items.tolist()):
+        xcd.setdefault((b, h), set()).add(g % 8)
+    assert all(len(x) == 1 for x in xcd.values())
 
 
 def test_plan_orders_longest_first(lib):
