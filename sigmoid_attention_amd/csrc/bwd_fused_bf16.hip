@@ -23,8 +23,8 @@ void bwd_kernel(const KArgs a, void* dq, int nq_items, int tiles_q) {
   const int g = remap_block(blockIdx.x, a.nitems + nq_items, a.xcd_chunk);
   bool dq_item = g >= a.nitems;
   Item it;
-  if (!VL && CAUSAL && a.nblocks > 0) {
-    it = decode_block_item(a, g, &dq_item);          // both passes' blocks, merged by cost
+  if (CAUSAL && a.nblocks > 0) {                    // both passes' blocks, merged by cost
+    it = VL ? varlen_block_item(a, g, &dq_item) : decode_block_item(a, g, &dq_item);
   } else if (!dq_item) {
     it = VL ? varlen_item(a, g, a.tiles_per_seq, 1) : decode_item(a, g, 0);
   } else {

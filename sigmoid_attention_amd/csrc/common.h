@@ -315,12 +315,12 @@ struct DirectPair {
 // Packed mode: the item's sequence bounds come from the device arrays cu_q / cu_k.
 // Packed-mode item g of a pass with T tiles per (sequence, head), over key rows or query
 // rows.
-__device__ __forceinline__ Item varlen_item(const KArgs& a, int g, int T, int over_keys) {
+__device__ __forceinline__ Item varlen_item_at(const KArgs& a, int b, int h, int t,
+                                               int over_keys) {
   Item it;
-  it.t = g % T;
-  const int bh = g / T;
-  it.h = bh % a.H;
-  it.b = bh / a.H;
+  it.t = t;
+  it.h = h;
+  it.b = b;
   const int q0 = a.cu_q[it.b], k0 = a.cu_k[it.b];
   it.nq = a.cu_q[it.b + 1] - q0;
   it.nk = a.cu_k[it.b + 1] - k0;
@@ -336,7 +336,29 @@ __device__ __forceinline__ Item varlen_item(const KArgs& a, int g, int T, int ov
   return it;
 }
 
+__device__ __forceinline__ Item varlen_item(const KArgs& a, int g, int T, int over_keys) {
+  const int bh = g / T;
+  return varlen_item_at(a, bh / a.H, bh % a.H, g % T, over_keys);
+}
+
+// Packed-mode item g of a block-major list (causal batches): block g / (B * H) holds one
+// tile of every (sequence, head); *dq_block is set for a dQ block of the one-call list.
+__device__ __forceinline__ Item varlen_block_item(const KArgs& a, int g, bool* dq_block) {
+  const int m = a.nsorted * a.H;
+  const int blk = g / m;
+  const int r = g - blk * m;
+  const unsigned code = a.blocks[blk];
+  *dq_block = (code & kDqBlock) != 0u;
+  const int b = r / a.H;
+  return varlen_item_at(a, b, r - b * a.H, (int)(code & (kDqBlock - 1u)),
+                        *dq_block ? 0 : a.tiles_over_keys);
+}
+
 __device__ __forceinline__ Item varlen_item(const KArgs& a, int g) {
+  if (a.nblocks > 0) {
+    bool dq_block;
+    return varlen_block_item(a, g, &dq_block);
+  }
   return varlen_item(a, g, a.tiles_per_seq, a.tiles_over_keys);
 }
 

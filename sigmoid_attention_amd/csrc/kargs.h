@@ -16,7 +16,9 @@
 // longest items first across the whole batch and not only within each sequence. In the
 // one-call backward the blocks of both passes are merged by cost. The remap is off in
 // this mode (blockIdx = item): with a multiple of 8 (sequence, head) pairs per block,
-// every tile of one head then lands on the same XCD.
+// every tile of one head then lands on the same XCD. Packed causal batches use the same
+// block-major order, with costs taken at the maximum lengths (the lengths themselves are
+// on the device).
 //
 // Packed variable-length batches (device-side cu_seqlens) use a third mode: the grid is
 // B x H x ceil(max_rows / tile) items in (b, h, tile) order with the tile fastest, each
@@ -55,7 +57,7 @@ struct KArgs {
   int32_t H;
   int32_t Lmax;
   int32_t nitems;        // compute items in the launch
-  int32_t nsorted;       // batch entries with n > 0
+  int32_t nsorted;       // batch entries with n > 0 (packed mode, block-major: B)
   int32_t tile;          // rows per item (queries for fwd/dq, keys for dk/dv)
   int32_t xcd_chunk;     // items per XCD per round; 0 disables the remap
   int32_t causal;
@@ -74,9 +76,10 @@ struct KArgs {
   const int32_t* cu_q;         // device [B + 1] query row bounds
   const int32_t* cu_k;         // device [B + 1] key row bounds
   const float* bias;           // device [B] or null (then beta_b = -ln(nk_b))
-  // block-major mode (nblocks > 0; padded causal batches of one length): item g is
-  // (sorted position, head) (g % (nsorted * H)) / H, g % H of block g / (nsorted * H),
-  // whose code holds the tile index (low 15 bits) and kDqBlock
+  // block-major mode (nblocks > 0; padded causal batches of one length, packed causal
+  // batches): item g is (sorted position or sequence, head) (g % (nsorted * H)) / H,
+  // g % H of block g / (nsorted * H), whose code holds the tile index (low 15 bits) and
+  // kDqBlock
   int32_t nblocks;
   uint16_t blocks[kMaxBlocks];
   int32_t off[kMaxBatch + 1];  // prefix item counts by sorted position

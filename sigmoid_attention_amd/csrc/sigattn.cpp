@@ -167,16 +167,16 @@ int xcd_chunk_default() {
   return v;
 }
 
-// 32 x 32 units of work in tile t of a causal sequence of n rows (tiles of `tile` rows,
-// one 32-row slice per wave): a query slice sees the keys up to its last row, a key
-// slice the queries from its first row on.
-double causal_tile_units(int n, int tile, int t, bool key_side) {
-  const int slices = (n + 31) / 32;
+// 32 x 32 units of work in tile t of a causal (nq, nk) pair, causal rule aligned at the
+// bottom right (tiles of `tile` rows, one 32-row slice per wave): a query slice sees the
+// keys up to its last row, a key slice the queries from its first row on.
+double causal_tile_units(int nq, int nk, int tile, int t, bool key_side) {
+  const int sq = (nq + 31) / 32, sk = (nk + 31) / 32;
   double u = 0.0;
   for (int w = 0; w < tile / 32; ++w) {
     const int r = t * (tile / 32) + w;
-    if (r >= slices) break;
-    u += key_side ? slices - r : r + 1;
+    if (r >= (key_side ? sk : sq)) break;
+    u += std::max(0, key_side ? std::min(sq, sk - r) : std::min(sk, r + 1 + sk - sq));
   }
   return u;
 }
@@ -185,30 +185,37 @@ double causal_tile_units(int n, int tile, int t, bool key_side) {
 // waves per SIMD), which orders the merged blocks of the one-call backward.
 constexpr double kDkdvUnitCost = 1.42;
 
-// Block-major list for a causal batch whose sequences all have one length: one block per
-// tile, costliest first. `which` is the pass (0 forward, 1 dQ, 2 dK/dV) or 3 for the
-// one-call backward, whose dK/dV and dQ blocks are merged by cost (dQ blocks flagged).
-// Other batches, and lists of more than kMaxBlocks blocks, keep the per-sequence order.
-void order_blocks(KArgs* a, int which) {
+// Block-major list of a causal batch: one block per tile, costliest first. `which` is the
+// pass (0 forward, 1 dQ, 2 dK/dV) or 3 for the one-call backward, whose dK/dV blocks (tk
+// key tiles) and dQ blocks (tq query tiles) are merged by cost, dQ blocks flagged. Lists
+// of more than kMaxBlocks blocks keep the default order.
+void set_blocks(KArgs* a, int which, int nq, int nk, int tq, int tk) {
   a->nblocks = 0;
-  if (!a->causal || a->nsorted == 0 || a->len[0] != a->len[a->nsorted - 1]) return;
-  const int n = a->len[0];
-  const int T = (n + a->tile - 1) / a->tile;
   struct Block { double cost; uint16_t code; };
   std::vector<Block> blocks;
   if (which == 2 || which == 3)
-    for (int t = 0; t < T; ++t)
-      blocks.push_back({kDkdvUnitCost * causal_tile_units(n, a->tile, t, true), (uint16_t)t});
+    for (int t = 0; t < tk; ++t)
+      blocks.push_back({kDkdvUnitCost * causal_tile_units(nq, nk, a->tile, t, true),
+                        (uint16_t)t});
   if (which != 2)
-    for (int t = T - 1; t >= 0; --t)
-      blocks.push_back({causal_tile_units(n, a->tile, t, false),
+    for (int t = tq - 1; t >= 0; --t)
+      blocks.push_back({causal_tile_units(nq, nk, a->tile, t, false),
                         (uint16_t)(t | (which == 3 ? sa::kDqBlock : 0u))});
-  if ((int)blocks.size() > sa::kMaxBlocks) return;
+  if (blocks.empty() || (int)blocks.size() > sa::kMaxBlocks) return;
   std::stable_sort(blocks.begin(), blocks.end(),
                    [](const Block& x, const Block& y) { return x.cost > y.cost; });
   a->nblocks = (int)blocks.size();
   for (int i = 0; i < a->nblocks; ++i) a->blocks[i] = blocks[i].code;
   a->xcd_chunk = 0;
+}
+
+// Padded batches: block-major only when causal and every listed sequence has one length.
+void order_blocks(KArgs* a, int which) {
+  a->nblocks = 0;
+  if (!a->causal || a->nsorted == 0 || a->len[0] != a->len[a->nsorted - 1]) return;
+  const int n = a->len[0];
+  const int T = (n + a->tile - 1) / a->tile;
+  set_blocks(a, which, n, n, T, T);
 }
 
 // Fill the kernel-argument block of one pass: the sorted, padded-tile-free work list.
@@ -429,6 +436,12 @@ void plan_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k
   a.out_f32 = p->out_dtype == SIGATTN_F32 ? 1 : 0;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = o0; a.out1 = o1;
   a.f16_pv = (pass == 0 && p->fast_math == 2) ? 1 : 0;
+  if (p->causal && p->B > 0) {
+    // block-major, costs at the maximum lengths; item g reads sequence (g % (B H)) / H
+    a.nsorted = p->B;
+    const int t = a.tiles_per_seq;
+    set_blocks(&a, pass, p->max_seqlen_q, p->max_seqlen_k, pass == 2 ? 0 : t, pass == 2 ? t : 0);
+  }
 }
 
 sigattn_status run_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k,
@@ -694,6 +707,8 @@ sigattn_status sigattn_bwd_varlen(const sigattn_varlen* p, const void* q, const 
   const int tiles_q = (int)((p->max_seqlen_q + tile - 1) / tile);
   const int nq_items = (int)((int64_t)p->B * p->H * tiles_q);
   if (a.nitems + nq_items == 0) return SIGATTN_OK;
+  if (p->causal)
+    set_blocks(&a, 3, p->max_seqlen_q, p->max_seqlen_k, tiles_q, a.tiles_per_seq);
   return sa::launch_bwd_bf16(a, dq, nq_items, tiles_q, p->causal != 0, p->gate != nullptr,
                              p->fast_math != 1, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? SIGATTN_OK : SIGATTN_ERR_HIP;
