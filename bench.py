@@ -7,7 +7,11 @@ One step = one pass of the whole hot path over one batch: sigattn_fwd, then siga
 Faster Training: Sigmoid Attention for single-cell Foundation Models"), n^2 pairs per
 head bidirectional, n(n+1)/2 causal. Inputs are resident in HBM before timing starts.
 The two backward passes are also timed alone, outside the timed step (sigattn_bwd_dq and
-sigattn_bwd_dkdv under "kernels").
+sigattn_bwd_dkdv under "kernels"). `ms_per_step` and `value` come from K steps between two
+events with nothing else in the stream; each call's duration (the per-kernel figures and
+`roofline`) from a second run of the same K steps with an event before and after each call.
+The host enqueues each timed loop while a spin kernel, ahead of the loop's first event,
+holds the GPU, so that short launches run back to back instead of at the host's pace.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_8k_s1]
                     [--no-cpu-baseline]
@@ -39,6 +43,9 @@ PEAK_HBM_GBS = 8000.0
 # recomputes S, forms dP, dV, dK (4 x 2d): 14 d per pair for the one-call backward. The
 # credited backward (2.5 x forward = 10 d) counts S and dP once.
 PASS_FLOPS_PER_PAIR = {"fwd": 4, "bwd": 14, "bwd_dq": 6, "bwd_dkdv": 8}
+TIMING = ("step: K steps between two HIP events, no other events in the stream; per call: "
+          "a second run of K steps with a HIP event before and after each call; each loop "
+          "is enqueued while a spin kernel ahead of its first event holds the GPU")
 
 
 def parse():
@@ -179,6 +186,50 @@ def decode_bytes(counts, H, d, out_bytes):
     return live * H * (2 * d * 2 + 4) + len(counts) * H * d * (2 + out_bytes)
 
 
+def hold_gpu(stream, steps):
+    """Keep the GPU busy (a spin kernel, before the first event) while the host enqueues a
+    timed loop, so that the loop's launches run back to back. Otherwise a loop of short
+    launches is paced by the host's launch path, and host time lands between events."""
+    import torch
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(min(steps, 400) * 1_000_000))   # about 0.5 ms per step at 2 GHz
+
+
+def time_steps(stream, steps, calls, step_time=True):
+    """K steps of `calls` (name -> function, run in order) on `stream`, timed twice: first
+    between two events with nothing else in the stream (the step time; skipped when
+    step_time is False), then again with an event before and after each call (each call's
+    duration, per step). The host enqueues each loop while the GPU is held busy."""
+    import torch
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    ms_step = None
+    if step_time:
+        start, end = ev(), ev()
+        torch.cuda.synchronize()
+        hold_gpu(stream, steps)
+        start.record(stream)
+        for _ in range(steps):
+            for fn in calls.values():
+                fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(end) / steps
+    evs = [[ev() for _ in range(len(calls) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    hold_gpu(stream, steps)
+    for e in evs:
+        for i, fn in enumerate(calls.values()):
+            e[i].record(stream)
+            fn()
+        e[-1].record(stream)
+    torch.cuda.synchronize()
+    per = {name: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, name in enumerate(calls)}
+    return ms_step, per
+
+
 def measure_decode(S, W, w, steps, warmup, no_cpu, cpu_seconds):
     import math
 
@@ -198,18 +249,9 @@ def measure_decode(S, W, w, steps, warmup, no_cpu, cpu_seconds):
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
         cache.decode(q, bias, out=out, out_dtype=torch.float32, workspace=ws)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for e in evs:
-        e[0].record(stream)
-        cache.decode(q, bias, out=out, out_dtype=torch.float32, workspace=ws)
-        e[1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / steps
-    ms_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_step, per = time_steps(stream, steps, {"decode": lambda: cache.decode(
+        q, bias, out=out, out_dtype=torch.float32, workspace=ws)})
+    ms_dec = float(np.mean(per["decode"]))
     counts = cache.count.cpu().numpy()
     nbytes = decode_bytes(counts, H, d, 4)
     res = {
@@ -219,7 +261,7 @@ def measure_decode(S, W, w, steps, warmup, no_cpu, cpu_seconds):
         "unit": "GB/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic", "timing": TIMING,
         "config": {"workload": w.name, "B": B, "H": H, "d": d, "cap": data["cap"],
                    "prefill_lengths": [int(x) for x in data["seqlens"]],
                    "live_entries": [int(x) for x in counts], "tau": w.tau, "sink": w.sink,
@@ -239,6 +281,8 @@ def measure_decode(S, W, w, steps, warmup, no_cpu, cpu_seconds):
         torch.mul(src, 2.0, out=dst)
     cp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(20)]
+    torch.cuda.synchronize()
+    hold_gpu(stream, 20)
     for e0, e1 in cp:
         e0.record(stream)
         torch.mul(src, 2.0, out=dst)
@@ -532,6 +576,7 @@ def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False):
                         torch.cuda.synchronize()
                     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                            for _ in range(iters)]
+                    hold_gpu(stream, iters)
                     for e0, e1 in evs:
                         e0.record(stream)
                         fn()
@@ -582,28 +627,10 @@ def measure_packed(S, W, w, data, stream, steps, warmup, out_dtype, fast_math):
         for fn in list(calls.values()) + list(alone.values()):
             fn()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for e in evs:
-        for i, fn in enumerate(calls.values()):
-            e[i].record(stream)
-            fn()
-        e[2].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / steps
-    per = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-           for i, name in enumerate(calls)}
+    ms_step, per_steps = time_steps(stream, steps, calls)
+    per = {name: float(np.mean(times)) for name, times in per_steps.items()}
     for name, fn in alone.items():
-        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        for e0, e1 in pe:
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        per[name] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pe]))
+        per[name] = float(np.mean(time_steps(stream, steps, {name: fn}, step_time=False)[1][name]))
     f_fwd = W.flops_forward(data["seqlens"], w.H, w.d, w.causal)
     f_bwd = W.flops_backward(data["seqlens"], w.H, w.d, w.causal)
     pairs = W.valid_pairs(data["seqlens"], w.causal) * w.H
@@ -619,7 +646,7 @@ def measure_packed(S, W, w, data, stream, steps, warmup, out_dtype, fast_math):
     return {
         "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "timing": TIMING,
         "config": {"workload": w.name, "layout": "packed rows, device cu_seqlens", "B": w.B,
                    "H": w.H, "d": w.d, "rows": int(sum(sl)), "seqlens": sl, "causal": w.causal,
                    "gated": w.gate is not None, "seed": w.seed,
@@ -645,34 +672,12 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math, s
     dk = torch.empty_like(o)
     dv = torch.empty_like(o)
 
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record(stream)
-        S.fwd(t["q"], t["k"], t["v"], sl, out=o, **kw)
-        if evs is not None:
-            evs[1].record(stream)
-        S.bwd(t["q"], t["k"], t["v"], t["do"], sl, out=(dq, dk, dv), **kw)
-        if evs is not None:
-            evs[2].record(stream)
-
+    calls = {"fwd": lambda: S.fwd(t["q"], t["k"], t["v"], sl, out=o, **kw),
+             "bwd": lambda: S.bwd(t["q"], t["k"], t["v"], t["do"], sl, out=(dq, dk, dv), **kw)}
     for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        step(evs[i])
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / steps
-    per = {"fwd": [], "bwd": []}
-    for e in evs:
-        per["fwd"].append(e[0].elapsed_time(e[1]))
-        per["bwd"].append(e[1].elapsed_time(e[2]))
+        for fn in calls.values():
+            fn()
+    ms_step, per = time_steps(stream, steps, calls)
 
     # each backward pass alone as well (outside the timed step): the two kernels that the
     # one-call backward runs in one launch
@@ -681,14 +686,7 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math, s
     for name, fn in (sep.items() if separate else ()):
         for _ in range(max(2, warmup // 4)):
             fn()
-        pairs_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    for _ in range(steps)]
-        for e0, e1 in pairs_ev:
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        per[name] = [e0.elapsed_time(e1) for e0, e1 in pairs_ev]
+        per[name] = time_steps(stream, steps, {name: fn}, step_time=False)[1][name]
 
     f_fwd = W.flops_forward(sl, w.H, w.d, w.causal)
     f_bwd = W.flops_backward(sl, w.H, w.d, w.causal)
@@ -716,7 +714,7 @@ def measure(S, W, w, t, gate, sl, stream, steps, warmup, out_dtype, fast_math, s
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic", "timing": TIMING,
         "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "Lmax": w.L,
                    "seqlens": [int(x) for x in sl], "causal": w.causal,
                    "gated": w.gate is not None, "seed": w.seed,
