@@ -105,7 +105,20 @@ struct Item {
 // blockIdx -> item index. Rounds of kNumXcd*chunk items; in each round XCD x (which
 // receives blocks w with w % 8 == x) takes the contiguous items [x*chunk, x*chunk+chunk).
 // Bijective; blocks past the last full round map to themselves.
+// chunk == kSnake (a block-major list that fits one round of resident workgroups): blocks
+// w, w + kNumCu, w + 2 kNumCu, ... share a CU under round-robin dispatch, so every second
+// span of kNumCu blocks takes its items in reverse order of groups of kNumXcd (a CU that
+// receives one of the costliest items receives cheaper ones in its other slots; the
+// order inside a group keeps each item's XCD). A last partial span maps to itself.
+constexpr int kNumCu = 256;
+constexpr int kSnake = -1;
 SA_HD inline int remap_block(int w, int nitems, int chunk) {
+  if (chunk == kSnake) {
+    const int span = w / kNumCu, base = span * kNumCu, c = w - base;
+    if ((span & 1) && base + kNumCu <= nitems)
+      return base + (kNumCu / kNumXcd - 1 - c / kNumXcd) * kNumXcd + c % kNumXcd;
+    return w;
+  }
   if (chunk <= 0) return w;
   const int round = kNumXcd * chunk;
   const int full = (nitems / round) * round;

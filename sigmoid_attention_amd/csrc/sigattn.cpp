@@ -209,6 +209,20 @@ void set_blocks(KArgs* a, int which, int nq, int nk, int tq, int tk) {
   a->xcd_chunk = 0;
 }
 
+// Workgroups of a pass resident on one CU (the kernels' waves per SIMD; a workgroup has
+// one wave on each of the CU's four SIMDs). Pass 3: the one-call backward.
+int slots_per_cu(int pass, int d) {
+  if (pass == 0) return d == 64 ? 3 : 2;
+  if (pass == 2) return d == 64 ? 2 : 1;
+  return 2;
+}
+
+// A block-major list that one round of resident workgroups holds is spread over the CUs
+// by the snake remap (remap_block); longer lists are list-scheduled in order.
+void snake_if_one_round(KArgs* a, int pass, int d, int nitems) {
+  if (a->nblocks > 0 && nitems <= sa::kNumCu * slots_per_cu(pass, d)) a->xcd_chunk = sa::kSnake;
+}
+
 // Padded batches: block-major only when causal and every listed sequence has one length.
 void order_blocks(KArgs* a, int which) {
   a->nblocks = 0;
@@ -259,6 +273,7 @@ void plan_pass(const sigattn_problem* p, int pass, KArgs* a) {
   a->out_f32 = p->out_dtype == SIGATTN_F32 ? 1 : 0;
   a->f16_pv = (pass == 0 && p->fast_math == 2) ? 1 : 0;
   order_blocks(a, pass);
+  snake_if_one_round(a, pass, p->d, a->nitems);
 }
 
 bool needs_zero_fill(const sigattn_problem* p) {
@@ -441,6 +456,7 @@ void plan_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k
     a.nsorted = p->B;
     const int t = a.tiles_per_seq;
     set_blocks(&a, pass, p->max_seqlen_q, p->max_seqlen_k, pass == 2 ? 0 : t, pass == 2 ? t : 0);
+    snake_if_one_round(&a, pass, p->d, a.nitems);
   }
 }
 
@@ -633,6 +649,7 @@ sigattn_status sigattn_bwd(const sigattn_problem* p, const void* q, const void* 
   KArgs a;
   plan_pass(p, 2, &a);
   order_blocks(&a, 3);
+  snake_if_one_round(&a, 3, p->d, 2 * a.nitems);
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.out0 = dk; a.out1 = dv;
   if (a.nitems > 0 && sa::launch_bwd_bf16(a, dq, a.nitems, 0, p->causal != 0, p->gate != nullptr,
                                           p->fast_math != 1, st) != hipSuccess)
@@ -707,8 +724,10 @@ sigattn_status sigattn_bwd_varlen(const sigattn_varlen* p, const void* q, const 
   const int tiles_q = (int)((p->max_seqlen_q + tile - 1) / tile);
   const int nq_items = (int)((int64_t)p->B * p->H * tiles_q);
   if (a.nitems + nq_items == 0) return SIGATTN_OK;
-  if (p->causal)
+  if (p->causal) {
     set_blocks(&a, 3, p->max_seqlen_q, p->max_seqlen_k, tiles_q, a.tiles_per_seq);
+    snake_if_one_round(&a, 3, p->d, a.nitems + nq_items);
+  }
   return sa::launch_bwd_bf16(a, dq, nq_items, tiles_q, p->causal != 0, p->gate != nullptr,
                              p->fast_math != 1, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? SIGATTN_OK : SIGATTN_ERR_HIP;
@@ -820,6 +839,7 @@ int64_t sigattn_plan(const sigattn_problem* p, int32_t pass, int32_t* items, int
   // the dK/dV pass's tiles), or both merged block-major; dQ items as (b, h, -1 - tile)
   order_blocks(&a, 3);
   const int total = 2 * a.nitems;
+  snake_if_one_round(&a, 3, p->d, total);
   for (int w = 0; w < total && w < cap; ++w) {
     const int g = sa::remap_block(w, total, a.xcd_chunk);
     bool dq_item = g >= a.nitems;

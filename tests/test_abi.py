@@ -207,14 +207,21 @@ def _causal_units(n, tile, t, key_side):
     return u
 
 
+def _item_cost(n, tile, t, pass_):
+    if pass_ == 3:
+        return _causal_units(n, tile, t, True) * 1.42 if t >= 0 else _causal_units(n, tile, -1 - t, False)
+    return _causal_units(n, tile, t, pass_ == 2)
+
+
 @pytest.mark.parametrize("pass_", [0, 1, 2, 3])
 def test_one_length_causal_batches_are_listed_tile_by_tile(lib, pass_):
-    """Causal batches of one length: each run of B * H consecutive items holds one tile
-    of every (sequence, head), the runs in non-increasing work (the one-call list weighs
-    a dK/dV unit 1.42 times a dQ unit), and item g runs on XCD g % 8, so that all tiles
-    of one head share an XCD when B * H is a multiple of 8."""
-    B, H, n = 4, 6, 1000
-    p, keep = S.make_problem(B, H, 1024, 64, [n] * B, causal=True)
+    """Causal batches of one length, more items than one round of resident workgroups:
+    each run of B * H consecutive items holds one tile of every (sequence, head), the
+    runs in non-increasing work (the one-call list weighs a dK/dV unit 1.42 times a dQ
+    unit), and item g runs on XCD g % 8, so that all tiles of one head share an XCD when
+    B * H is a multiple of 8."""
+    B, H, n = 8, 12, 2048
+    p, keep = S.make_problem(B, H, 2048, 64, [n] * B, causal=True)
     items, tile = S.plan(p, pass_)
     m = B * H
     T = -(-n // tile)
@@ -224,17 +231,31 @@ def test_one_length_causal_batches_are_listed_tile_by_tile(lib, pass_):
         run = items[blk * m:(blk + 1) * m]
         assert sorted((b, h) for b, h, _ in run.tolist()) == [(b, h) for b in range(B) for h in range(H)]
         assert len(set(run[:, 2].tolist())) == 1
-        t = int(run[0, 2])
-        if pass_ == 3:
-            key_side = t >= 0
-            t = t if key_side else -1 - t
-            costs.append(_causal_units(n, tile, t, key_side) * (1.42 if key_side else 1.0))
-        else:
-            costs.append(_causal_units(n, tile, t, pass_ == 2))
+        costs.append(_item_cost(n, tile, int(run[0, 2]), pass_))
     assert costs == sorted(costs, reverse=True)
     xcd = {}
     for g, (b, h, _) in enumerate(items.tolist()):
         xcd.setdefault((b, h), set()).add(g % 8)
+    assert all(len(x) == 1 for x in xcd.values())
+
+
+def test_one_round_causal_forward_spreads_work_over_cus(lib):
+    """A causal one-length forward that one round of resident workgroups holds (16 x 12
+    heads x 4 tiles of 512 rows; three per CU): launch positions w, w + 256, w + 512 share
+    a CU under round-robin dispatch, and every second span of 256 takes its items in
+    reverse order of groups of 8, so the busiest CU carries at most 8 % more work than
+    the average (24 % more in plain list order) while each head keeps its XCD."""
+    B, H, n = 16, 12, 512
+    p, keep = S.make_problem(B, H, 512, 64, [n] * B, causal=True)
+    items, tile = S.plan(p, 0)
+    assert len(items) == 768
+    per_cu = np.zeros(256)
+    for w, (b, h, t) in enumerate(items.tolist()):
+        per_cu[w % 256] += _causal_units(n, tile, t, False)
+    assert per_cu.max() <= 1.08 * per_cu.mean()
+    xcd = {}
+    for w, (b, h, _) in enumerate(items.tolist()):
+        xcd.setdefault((b, h), set()).add(w % 8)
     assert all(len(x) == 1 for x in xcd.values())
 
 
