@@ -75,6 +75,9 @@ def parse():
                     help="the pages' kernel sweep: L = 512..16384 at B*L = 16384 tokens, d = 64 "
                          "(32 heads) and 128 (16 heads), 0 %% and 25 %% padding; forward and "
                          "backward TFLOPS, mean and 99 %% interval over 250 iterations")
+    ap.add_argument("--causal", action="store_true",
+                    help="with --sweep: causal attention, every sequence at full length "
+                         "(no padding)")
     ap.add_argument("--packed", action="store_true",
                     help="run the workload's sequences packed (device cu_seqlens, no padding) "
                          "through sigattn_fwd_varlen and sigattn_bwd_varlen")
@@ -442,7 +445,8 @@ def main():
     S.load()
     if args.sweep:
         print(json.dumps(sweep(S, W, iters=250,
-                               fast_math=1 if args.fast_math else (2 if args.f16_forward else 0))))
+                               fast_math=1 if args.fast_math else (2 if args.f16_forward else 0),
+                               causal=args.causal)))
         return
     w = W.WORKLOADS[args.workload]
     if w.name.startswith("decode"):
@@ -534,29 +538,31 @@ def padding_loss(S, W, stream, steps, warmup, out_dtype, fast_math):
     return out
 
 
-def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False):
+def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False, causal=False):
     """The kernel sweep of the sigmoid-attention paper's section 4.1 ("Kernel
     Performance"): sequence length 512..16384 with the batch set so that B * L = 16384
     tokens, head dimension 64 (32 heads) and 128 (16 heads) of a 2048-wide model, 0 % and
     25 % padding; bidirectional. Per configuration the forward and the backward
     (sigattn_bwd: dQ and dK/dV kernels) are timed separately, each for `iters` iterations after about
     `warmup_ms` of warm-up, with a pair of HIP events per iteration on the launch stream;
-    TFLOPS count valid tokens only."""
+    TFLOPS count valid tokens only. causal: the same grid with the causal mask and every
+    sequence at full length (FLOPs over the n(n+1)/2 allowed pairs)."""
     import torch
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     rows = []
     for d, H in ((64, 32), (128, 16)):
-        for pad in (0.0, 0.25):
+        for pad in ((0.0,) if causal else (0.0, 0.25)):
             for L in (512, 1024, 2048, 4096, 8192, 16384):
                 B = 16384 // L
                 w = W.Workload(f"sweep_L{L}_d{d}_p{int(pad * 100)}", "bf16", B, H, d, L,
-                               ("mean_pad", pad), seed=1000 + L + d + int(pad * 100))
+                               ("mean_pad", pad), seed=1000 + L + d + int(pad * 100),
+                               causal=causal)
                 data = W.generate(w)
                 t = {k: torch.from_numpy(data[k]).to(torch.bfloat16).to(dev)
                      for k in ("q", "k", "v", "do")}
                 sl = data["seqlens"]
-                kw = dict(out_dtype=torch.float32, fast_math=fast_math)
+                kw = dict(out_dtype=torch.float32, fast_math=fast_math, causal=causal)
                 o = torch.empty(t["q"].shape, dtype=torch.float32, device=dev)
                 dq, dk, dv = torch.empty_like(o), torch.empty_like(o), torch.empty_like(o)
 
@@ -568,8 +574,8 @@ def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False):
 
                 res = {"L": L, "B": B, "H": H, "d": d, "padding": pad,
                        "seqlens": [int(x) for x in sl]}
-                for name, fn, flops in (("fwd", fwd, W.flops_forward(sl, H, d, False)),
-                                        ("bwd", bwd, W.flops_backward(sl, H, d, False))):
+                for name, fn, flops in (("fwd", fwd, W.flops_forward(sl, H, d, causal)),
+                                        ("bwd", bwd, W.flops_backward(sl, H, d, causal))):
                     t0 = time.perf_counter()
                     while time.perf_counter() - t0 < warmup_ms * 1e-3:
                         fn()
@@ -590,7 +596,9 @@ def sweep(S, W, iters=250, warmup_ms=100.0, fast_math=False):
                 rows.append(res)
                 print(f"[sweep] d={d} pad={pad} L={L} B={B}: fwd {res['fwd']['tflops']:.1f} "
                       f"bwd {res['bwd']['tflops']:.1f} TFLOPS", file=sys.stderr, flush=True)
-    return {"sweep": "kernel sweep, B*L = 16384 tokens, bidirectional, bf16 inputs, float "
+    return {"sweep": "kernel sweep, B*L = 16384 tokens, "
+                     + ("causal, full-length sequences" if causal else "bidirectional")
+                     + ", bf16 inputs, float "
                      "outputs, " + ["hi+lo operands", "single bf16 operands",
                                     "f16 forward P V, hi+lo backward"][int(fast_math)],
             "iters": iters, "rows": rows}
