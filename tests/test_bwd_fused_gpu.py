@@ -60,6 +60,22 @@ def test_bitwise_equal_to_separate_passes(d, variant, fast):
         _assert_bitwise(torch, fused, sep, f"d={d} {variant} fast={fast} out={od}")
 
 
+@pytest.mark.parametrize("variant", ["causal", "causal_gated_drop"])
+@pytest.mark.parametrize("shape", [(16, 12, 512), (5, 3, 700), (2, 4, 4096)])
+def test_one_length_causal_bitwise(shape, variant):
+    """Causal batches of one length: the one-call list merges both passes' tile blocks by
+    cost (the separate passes take their own block orders); bitwise the same results."""
+    torch = need_gpu()
+    B, H, L = shape
+    w = W.Workload(f"fused_one_length_{variant}_{B}x{H}_{L}", "bf16", B, H, 64, L,
+                   ("fixed", [L] * B), seed=640 + B + L, **VARIANTS[variant])
+    data = W.generate(w)
+    note(f"one-call backward, one length {B}x{H}x{L} {variant}")
+    for od in (torch.float32, torch.bfloat16):
+        fused, sep = _both(torch, data, out_dtype=od)
+        _assert_bitwise(torch, fused, sep, f"one length {shape} {variant} out={od}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_against_oracle(d):
     torch = need_gpu()

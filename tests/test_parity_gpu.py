@@ -87,6 +87,34 @@ def test_lengths_at_chunk_multiples(d, variant):
     print(check_all(gpu, oracle_full(data), data["seqlens"], BF16_TOL, f"chunks {variant} {d}"))
 
 
+ONE_LENGTH = [(64, 16, 8, 512), (128, 16, 8, 512), (64, 5, 3, 700), (128, 5, 3, 700)]
+
+
+@pytest.mark.parametrize("d,B,H,L", ONE_LENGTH)
+def test_one_length_causal_full(d, B, H, L):
+    """Causal gated batches whose sequences share one length take block-major work lists
+    (and, for 16 x 8 heads of 512 rows, the snake placement of a one-round forward);
+    every pass, and the one-call backward, against the full oracle."""
+    torch = need_gpu()
+    w = W.Workload(f"one_length_{d}_{B}x{H}_{L}", "bf16", B, H, d, L, ("fixed", [L] * B),
+                   seed=40 + d + L, causal=True, gate=("logistic_normal", 2.0, 2.0, 0.2, 0.01),
+                   tau=0.05, sink=4)
+    data = W.generate(w)
+    ref = oracle_full(data)
+    note(f"one-length causal d={d} B={B} H={H} L={L}: separate passes")
+    gpu = run_gpu(data, torch.bfloat16, out_dtype=torch.float32)
+    print(check_all(gpu, ref, data["seqlens"], BF16_TOL, f"one-length {d} {B}x{H} {L}"))
+    note(f"one-length causal d={d} B={B} H={H} L={L}: one-call backward")
+    import sigmoid_attention_amd as S
+    from gpu_util import kwargs_of, to_device
+    t = to_device(data, torch.bfloat16)
+    dq, dk, dv = S.bwd(t["q"], t["k"], t["v"], t["do"], data["seqlens"],
+                       out_dtype=torch.float32, **kwargs_of(data, t["gate"]))
+    torch.cuda.synchronize()
+    fused = {"dQ": dq.cpu().numpy(), "dK": dk.cpu().numpy(), "dV": dv.cpu().numpy()}
+    print(check_all(fused, ref, data["seqlens"], BF16_TOL, f"one-length one-call {d}"))
+
+
 @pytest.mark.parametrize("name", ["causal_gated_512", "causal_forced_drop_512"])
 def test_causal_gated_full(name):
     """Causal GPT-2-shaped gated layer (B=16, H=12, d=64, L=512) against the full oracle."""
