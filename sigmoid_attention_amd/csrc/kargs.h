@@ -14,9 +14,11 @@
 // listed block-major instead: one block per tile index, holding that tile of every
 // (sequence, head), the blocks in decreasing cost, so that list scheduling starts the
 // longest items first across the whole batch and not only within each sequence. In the
-// one-call backward the blocks of both passes are merged by cost. The remap is off in
-// this mode (blockIdx = item): with a multiple of 8 (sequence, head) pairs per block,
-// every tile of one head then lands on the same XCD. Packed causal batches use the same
+// one-call backward the blocks of both passes are merged by cost. The XCD remap is off in
+// this mode (blockIdx = item, or the snake placement of remap_block when one round of
+// resident workgroups holds the list, which keeps each item's XCD): with a multiple of 8
+// (sequence, head) pairs per block, every tile of one head then lands on the same XCD,
+// XCD g mod 8. Packed causal batches use the same
 // block-major order, with costs taken at the maximum lengths (the lengths themselves are
 // on the device).
 //
