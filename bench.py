@@ -194,8 +194,11 @@ def hold_gpu(stream, steps):
     timed loop, so that the loop's launches run back to back. Otherwise a loop of short
     launches is paced by the host's launch path, and host time lands between events."""
     import torch
+    spin = getattr(torch.cuda, "_sleep", None)   # torch's spin kernel (a private helper)
+    if spin is None:
+        return
     with torch.cuda.stream(stream):
-        torch.cuda._sleep(int(min(steps, 400) * 1_000_000))   # about 0.5 ms per step at 2 GHz
+        spin(int(min(steps, 400) * 1_000_000))   # about 0.5 ms per step at 2 GHz
 
 
 def time_steps(stream, steps, calls, step_time=True):
