@@ -83,12 +83,16 @@ struct KArgs {
   // g % H of block g / (nsorted * H), whose code holds the tile index (low 15 bits) and
   // kDqBlock
   int32_t nblocks;
-  uint16_t blocks[kMaxBlocks];
+  uint32_t blocks[kMaxBlocks];   // one dword each: read with a scalar load
   int32_t off[kMaxBatch + 1];  // prefix item counts by sorted position
   float c2[kMaxBatch];         // -beta * log2(e) by sorted position
-  uint16_t len[kMaxBatch];     // valid length by sorted position
-  uint8_t bidx[kMaxBatch];     // batch index by sorted position
+  // valid length << 8 | batch index, by sorted position: one dword per entry, so that
+  // the work-item decode reads it with a scalar load (through the scalar cache)
+  uint32_t lenb[kMaxBatch];
 };
+
+SA_HD inline int len_at(const KArgs& a, int p) { return (int)(a.lenb[p] >> 8); }
+SA_HD inline int bidx_at(const KArgs& a, int p) { return (int)(a.lenb[p] & 0xffu); }
 
 struct Item {
   int b;         // batch index
@@ -133,8 +137,8 @@ SA_HD inline int remap_block(int w, int nitems, int chunk) {
 // Item (head h, tile t) of the sequence at sorted position p.
 SA_HD inline Item item_at(const KArgs& a, int p, int h, int t) {
   Item it;
-  it.b = a.bidx[p];
-  it.nq = it.nk = a.len[p];
+  it.b = bidx_at(a, p);
+  it.nq = it.nk = len_at(a, p);
   it.diag = 0;
   it.valid = 1;
   it.c2 = a.c2[p];
@@ -170,7 +174,7 @@ SA_HD inline Item decode_item(const KArgs& a, int g, int reverse) {
     if (a.off[mid] <= g) lo = mid; else hi = mid - 1;
   }
   const int p = lo;
-  const int T = (a.len[p] + a.tile - 1) / a.tile;
+  const int T = (len_at(a, p) + a.tile - 1) / a.tile;
   const int local = g - a.off[p];
   int h, t;
   if (a.causal) {

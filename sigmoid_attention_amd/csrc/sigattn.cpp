@@ -191,16 +191,16 @@ constexpr double kDkdvUnitCost = 1.42;
 // of more than kMaxBlocks blocks keep the default order.
 void set_blocks(KArgs* a, int which, int nq, int nk, int tq, int tk) {
   a->nblocks = 0;
-  struct Block { double cost; uint16_t code; };
+  struct Block { double cost; uint32_t code; };
   std::vector<Block> blocks;
   if (which == 2 || which == 3)
     for (int t = 0; t < tk; ++t)
       blocks.push_back({kDkdvUnitCost * causal_tile_units(nq, nk, a->tile, t, true),
-                        (uint16_t)t});
+                        (uint32_t)t});
   if (which != 2)
     for (int t = tq - 1; t >= 0; --t)
       blocks.push_back({causal_tile_units(nq, nk, a->tile, t, false),
-                        (uint16_t)(t | (which == 3 ? sa::kDqBlock : 0u))});
+                        (uint32_t)t | (which == 3 ? sa::kDqBlock : 0u)});
   if (blocks.empty() || (int)blocks.size() > sa::kMaxBlocks) return;
   std::stable_sort(blocks.begin(), blocks.end(),
                    [](const Block& x, const Block& y) { return x.cost > y.cost; });
@@ -226,8 +226,9 @@ void snake_if_one_round(KArgs* a, int pass, int d, int nitems) {
 // Padded batches: block-major only when causal and every listed sequence has one length.
 void order_blocks(KArgs* a, int which) {
   a->nblocks = 0;
-  if (!a->causal || a->nsorted == 0 || a->len[0] != a->len[a->nsorted - 1]) return;
-  const int n = a->len[0];
+  if (!a->causal || a->nsorted == 0 || sa::len_at(*a, 0) != sa::len_at(*a, a->nsorted - 1))
+    return;
+  const int n = sa::len_at(*a, 0);
   const int T = (n + a->tile - 1) / a->tile;
   set_blocks(a, which, n, n, T, T);
 }
@@ -248,8 +249,7 @@ void plan_pass(const sigattn_problem* p, int pass, KArgs* a) {
     const int n = p->seqlens[b];
     const int T = (n + tile - 1) / tile;
     a->off[i + 1] = a->off[i] + p->H * T;
-    a->len[i] = (uint16_t)n;
-    a->bidx[i] = (uint8_t)b;
+    a->lenb[i] = ((uint32_t)n << 8) | (uint32_t)b;
     a->c2[i] = (float)(-beta_of(p, b) * kLog2eD);
   }
   a->nitems = a->off[a->nsorted];
