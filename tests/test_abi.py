@@ -239,6 +239,27 @@ def test_one_length_causal_batches_are_listed_tile_by_tile(lib, pass_):
     assert all(len(x) == 1 for x in xcd.values())
 
 
+@pytest.mark.parametrize("n,expect_blocks", [(1, True), (128, True), (8192, True),
+                                              (8193, False)])
+def test_one_call_list_block_limit(lib, n, expect_blocks):
+    """The one-call list of a causal one-length batch is block-major up to 128 tile blocks
+    (two passes of 64 tiles: n = 8192); one tile more keeps the per-sequence order. Both
+    cover every tile of both passes exactly once."""
+    B, H = 2, 3
+    p, keep = S.make_problem(B, H, n, 64, [n] * B, causal=True)
+    items, tile = S.plan(p, 3)
+    T = -(-n // tile)
+    want = sorted((b, h, t) for b in range(B) for h in range(H) for t in range(T))
+    got = items.tolist()
+    assert sorted(tuple(x) for x in got if x[2] >= 0) == want
+    assert sorted((b, h, -1 - t) for b, h, t in got if t < 0) == want
+    # block-major: the first B * H items are one tile of every (sequence, head)
+    first = items[:B * H]
+    is_block = (len(set(first[:, 2].tolist())) == 1
+                and sorted((b, h) for b, h, _ in first.tolist()) == [(b, h) for b in range(B) for h in range(H)])
+    assert is_block == expect_blocks or T == 1
+
+
 def test_one_round_causal_forward_spreads_work_over_cus(lib):
     """A causal one-length forward that one round of resident workgroups holds (16 x 12
     heads x 4 tiles of 512 rows; three per CU): launch positions w, w + 256, w + 512 share

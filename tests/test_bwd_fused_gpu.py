@@ -61,10 +61,13 @@ def test_bitwise_equal_to_separate_passes(d, variant, fast):
 
 
 @pytest.mark.parametrize("variant", ["causal", "causal_gated_drop"])
-@pytest.mark.parametrize("shape", [(16, 12, 512), (5, 3, 700), (2, 4, 4096)])
+@pytest.mark.parametrize("shape", [(16, 12, 512), (5, 3, 700), (2, 4, 4096), (1, 2, 8193),
+                                   (3, 1, 1)])
 def test_one_length_causal_bitwise(shape, variant):
     """Causal batches of one length: the one-call list merges both passes' tile blocks by
-    cost (the separate passes take their own block orders); bitwise the same results."""
+    cost (the separate passes take their own block orders); bitwise the same results.
+    At 8193 rows the one-call list (130 tile blocks) keeps the per-sequence order while
+    the separate passes (65 each) are block-major."""
     torch = need_gpu()
     B, H, L = shape
     w = W.Workload(f"fused_one_length_{variant}_{B}x{H}_{L}", "bf16", B, H, 64, L,
