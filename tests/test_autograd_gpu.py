@@ -63,6 +63,26 @@ def test_autograd_matches_direct_calls(d, case, gate_grad):
         assert g.grad is None
 
 
+@pytest.mark.parametrize("fast_math", [1, 2])
+def test_autograd_fast_modes_match_direct_calls(fast_math):
+    """The precision modes pass through: single bf16 operands (1) and the f16 forward (2)
+    give bitwise the direct calls' results under autograd too."""
+    torch = need_gpu()
+    import sigmoid_attention_amd as S
+    w, data, t, gate = _inputs(torch, "causal_gated", 64)
+    note(f"autograd fast_math={fast_math}")
+    kw = dict(causal=True, tau=w.tau, sink=w.sink, gate=gate, fast_math=fast_math)
+    q, k, v = (t[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    o = S.attention(q, k, v, data["seqlens"], out_dtype=torch.float32, **kw)
+    o.backward(t["do"].float())
+    o_ref = S.fwd(t["q"], t["k"], t["v"], data["seqlens"], out_dtype=torch.float32, **kw)
+    refs = S.bwd(t["q"], t["k"], t["v"], t["do"], data["seqlens"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for name, got, ref in zip(("dQ", "dK", "dV"), (q.grad, k.grad, v.grad), refs):
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), name
+
+
 def test_autograd_against_oracle():
     """Float output of the forward at the bar; the bf16 gradients within the element-wise
     bounds that add their own bf16 rounding (the bounds the parity tests use for bf16
