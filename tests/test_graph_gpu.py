@@ -55,11 +55,13 @@ def _gate(torch, rng, B, L):
     return torch.from_numpy(g.astype(np.float32)).cuda()
 
 
+@pytest.mark.parametrize("lengths", ["ragged", "one_length"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_padded_step_replays(d):
+def test_padded_step_replays(d, lengths):
+    """Ragged lengths take the per-sequence work lists, one length the block-major ones."""
     torch = need_gpu()
     B, H, L = 3, 2, 200
-    sl = [200, 77, 1]
+    sl = [200, 77, 1] if lengths == "ragged" else [200, 200, 200]
     kw = dict(causal=True, tau=0.05, sink=4)
     rng = np.random.default_rng(40 + d)
     x = {n: _bf16(torch, rng, (B, H, L, d)) for n in ("q", "k", "v", "do")}
@@ -71,7 +73,7 @@ def test_padded_step_replays(d):
         S.fwd(x["q"], x["k"], x["v"], sl, gate=gate, out=o, out_dtype=torch.float32, **kw)
         S.bwd(x["q"], x["k"], x["v"], x["do"], sl, gate=gate, out=grads, **kw)
 
-    note(f"graph capture: padded fwd + bwd d={d}")
+    note(f"graph capture: padded fwd + bwd d={d} {lengths}")
     graph = _capture(torch, step)
     for r in range(REPLAYS):
         if r:
