@@ -91,6 +91,9 @@ struct KArgs {
   uint32_t lenb[kMaxBatch];
 };
 
+// passed by value as the kernels' argument: stay within the 4 KiB a launch carries
+static_assert(sizeof(KArgs) <= 4096, "kernel-argument block above 4 KiB");
+
 SA_HD inline int len_at(const KArgs& a, int p) { return (int)(a.lenb[p] >> 8); }
 SA_HD inline int bidx_at(const KArgs& a, int p) { return (int)(a.lenb[p] & 0xffu); }
 
