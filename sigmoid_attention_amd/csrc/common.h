@@ -268,8 +268,8 @@ struct DirectPair {
   static constexpr int CPR = D / 8;
   static constexpr int TILE = ROWS * D * 2;
   static constexpr int ROWS_APART = NWAVES * 64 / CPR;   // rows between this wave's blocks
-  static_assert(Tile::PER_WAVE == 2, "two blocks per wave and tile");
-  static_assert(ROWS_APART % 16 == 0, "the two blocks must share the low four row bits");
+  static_assert(Tile::PER_WAVE % 2 == 0, "pairs of blocks per wave and tile");
+  static_assert(ROWS_APART % 16 == 0, "this wave's blocks must share the low four row bits");
   uint32_t voff;       // per-lane byte offset of block 0 within an interior tile
   uint32_t rb;         // row stride in bytes
   int w;               // wave index (uniform)
@@ -283,16 +283,24 @@ struct DirectPair {
     voff = (uint32_t)row * rb + (uint32_t)(((P % CPR) ^ xsw<D>(row)) * 16);
   }
 
+  // Block i of this wave (i = 0 .. PER_WAVE - 1) lies i * ROWS_APART rows further in the
+  // source and i * NWAVES KB further in LDS, with the same per-lane offset.
   __device__ __forceinline__ void fast(const char* base, uint32_t lds) const {
-    const uint64_t b0 = uniform_u64(reinterpret_cast<uintptr_t>(base));
-    const uint64_t b1 = uniform_u64(b0 + (uint64_t)ROWS_APART * rb);
-    const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds);
-    const uint32_t lds1 = (uint32_t)__builtin_amdgcn_readfirstlane(lds + (uint32_t)NWAVES * 1024u);
-    // 5 wait states between a vector write of an SGPR operand and the memory instruction
-    // reading it (once for both loads), 1 between the SALU write of M0 and the LDS DMA
-    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %3\n\t"
-                 "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4"
-                 :: "v"(voff), "s"(lds0), "s"(lds1), "s"(b0), "s"(b1) : "memory");
+#pragma unroll
+    for (int pr = 0; pr < Tile::PER_WAVE / 2; ++pr) {
+      const uint64_t b0 = uniform_u64(reinterpret_cast<uintptr_t>(base) +
+                                      (uint64_t)(2 * pr * ROWS_APART) * rb);
+      const uint64_t b1 = uniform_u64(b0 + (uint64_t)ROWS_APART * rb);
+      const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+          lds + (uint32_t)(2 * pr * NWAVES) * 1024u);
+      const uint32_t lds1 = (uint32_t)__builtin_amdgcn_readfirstlane(
+          lds + (uint32_t)((2 * pr + 1) * NWAVES) * 1024u);
+      // 5 wait states between a vector write of an SGPR operand and the memory instruction
+      // reading it (once for both loads), 1 between the SALU write of M0 and the LDS DMA
+      asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %3\n\t"
+                   "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4"
+                   :: "v"(voff), "s"(lds0), "s"(lds1), "s"(b0), "s"(b1) : "memory");
+    }
   }
 
   // rows row_base .. row_base + ROWS - 1 of a and b into the stage at lds_stage

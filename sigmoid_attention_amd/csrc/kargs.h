@@ -57,7 +57,7 @@ struct KArgs {
   int64_t sb, sh, sl;    // element strides of the 4-D tensors
   int64_t gsb;           // gate batch stride (elements)
   int32_t H;
-  int32_t Lmax;
+  int32_t Lmax;          // padded length (packed mode: the longest query row count)
   int32_t nitems;        // compute items in the launch
   int32_t nsorted;       // batch entries with n > 0 (packed mode, block-major: B)
   int32_t tile;          // rows per item (queries for fwd/dq, keys for dk/dv)

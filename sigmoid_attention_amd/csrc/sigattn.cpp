@@ -433,6 +433,7 @@ void plan_varlen(const sigattn_varlen* p, int pass, const void* q, const void* k
   a.tiles_per_seq = (int32_t)((rows + tile - 1) / tile);
   a.tiles_over_keys = pass == 2 ? 1 : 0;
   a.nitems = (int32_t)((int64_t)p->B * p->H * a.tiles_per_seq);
+  a.Lmax = p->max_seqlen_q;   // packed mode: the longest query row count (kernel choice)
   a.cu_q = p->cu_seqlens_q;
   a.cu_k = p->cu_seqlens_k;
   a.bias = p->bias;

@@ -87,6 +87,19 @@ def test_lengths_at_chunk_multiples(d, variant):
     print(check_all(gpu, oracle_full(data), data["seqlens"], BF16_TOL, f"chunks {variant} {d}"))
 
 
+@pytest.mark.parametrize("variant", ["bidir", "causal_gated_drop"])
+def test_d128_long_query_tiles(variant):
+    """d = 128 batches whose longest sequence reaches 1024 query rows run the dK/dV pass
+    with 64-row query tiles; full comparison with a ragged partner sequence."""
+    torch = need_gpu()
+    w = W.Workload(f"d128_long_tiles_{variant}", "bf16", 2, 2, 128, 1100, ("fixed", [1100, 301]),
+                   seed=77, **SMALL_VARIANTS[variant])
+    data = W.generate(w)
+    note(f"d=128 long query tiles {variant}")
+    gpu = run_gpu(data, torch.bfloat16, out_dtype=torch.float32)
+    print(check_all(gpu, oracle_full(data), data["seqlens"], BF16_TOL, f"d128 long {variant}"))
+
+
 ONE_LENGTH = [(64, 16, 8, 512), (128, 16, 8, 512), (64, 5, 3, 700), (128, 5, 3, 700)]
 
 
